@@ -1,0 +1,211 @@
+"""Benchmark of the MXFP8 x MXFP4 MoE expert layer on one MI355X.
+
+A step is one full layer call (route, quant, permute, FC1 + SiTU + requant,
+FC2 + combine) over one batch of synthetic input already resident in HBM.
+Default workload: the decode batch (T = 8 tokens, H = 7168, I = 3584,
+896 experts, top-16).  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_T8]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense MXFP8-rate scaled MFMA (f8 x f4 issues at this rate)
+
+WORKLOADS = {"tiny": 0, "decode_T8": 1, "batched_decode_T256": 2, "prefill_T8192": 3,
+             "ep_share_T4096": 4}
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def _traffic(kernel_src, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "fc1_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        rec = d.get(workload)
+        if rec and rec.get("source_sha256") == _sha(kernel_src):
+            return rec["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+    return None
+
+
+def cpu_baseline(cfg, act, weights_dev, topk_idx, topk_w, n_tokens=1):
+    """The oracle, as it stands, on a bounded sample: the first n tokens of the
+    workload, evaluated route by route.  Returns tokens/s and threads used."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    def weight_fn(e):
+        return tuple(weights_dev[k][e].cpu().numpy() for k in ("w13", "w13_s", "w2", "w2_s"))
+
+    t0 = time.perf_counter()
+    oracle.oracle_tokens(list(range(n_tokens)), act["x_bf16"][:n_tokens], topk_idx, topk_w,
+                         weight_fn, top_k=cfg.K, expert_offset=cfg.expert_offset,
+                         E_local=cfg.E_local)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return n_tokens / dt, threads, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_T8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import mxfp8_mxfp4_experts_amd as m
+    import synth
+
+    cfg = synth.CONFIGS[WORKLOADS[args.workload]]
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    if cfg.H == 7168:
+        wcfg = synth.custom_config("w", 0, T=1, H=cfg.H, I=cfg.I, E=cfg.E, K=1, E_local=cfg.E)
+        w_all = synth.make_expert_weights(wcfg, device=dev)
+        sl = slice(cfg.expert_offset, cfg.expert_offset + cfg.E_local)
+        w = {k: v[sl] for k, v in w_all.items()}
+    else:
+        w = {k: v.to(dev) for k, v in synth.make_expert_weights(cfg, device="cpu").items()}
+    act = synth.make_activations(cfg)
+    x = torch.from_numpy(act["x_bf16"].astype(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(act["logits"]).to(dev)
+    bias = torch.from_numpy(act["bias"]).to(dev)
+    layer = m.MoELayer(w["w13"], w["w13_s"], w["w2"], w["w2_s"], top_k=cfg.K, E=cfg.E,
+                       expert_offset=cfg.expert_offset, max_tokens=cfg.T)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s workload={args.workload}",
+          file=sys.stderr, flush=True)
+
+    B = m._binding
+    K, T, H, I, E_local = cfg.K, cfg.T, cfg.H, cfg.I, cfg.E_local
+    R = T * K
+    idx, tw = layer.topk_idx[:T], layer.topk_w[:T]
+    xq, xs = layer.xq[:T], layer.xs[:T]
+    sroute, rrow = layer.sorted_route[:R], layer.route_row[:R]
+    hq, hs = layer.hq[:R], layer.hs[:R]
+
+    def step(ev=None):
+        B.moe_route(logits, bias, K, cfg.routed_scaling, idx, tw)
+        B.moe_quant_mxfp8(x, xq, xs)
+        B.moe_permute(idx, cfg.expert_offset, E_local, layer.workspace, layer.expert_offsets,
+                      sroute, rrow)
+        if ev is not None:
+            ev[0].record()
+        B.moe_fc1_situ(xq, xs, K, layer.expert_offsets, sroute, layer.w13, layer.w13_s,
+                       layer.workspace, cfg.situ_alpha, cfg.situ_beta, hq, hs)
+        if ev is not None:
+            ev[1].record()
+        B.moe_fc2_combine(hq, hs, T, K, layer.expert_offsets, rrow, tw, layer.w2, layer.w2_s,
+                          layer.workspace, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # Algorithmic work of this batch.
+    offs = layer.expert_offsets.cpu().numpy()
+    n_kept = int(offs[-1])
+    D = int(np.count_nonzero(np.diff(offs)))
+    rr = rrow.cpu().numpy().reshape(T, K)
+    tokens_used = int(np.count_nonzero((rr >= 0).any(1)))
+    w13_bytes = 2 * I * H * (1 / 2 + 1 / 32)
+    fc1_bytes = D * w13_bytes + tokens_used * H * (1 + 1 / 32) + n_kept * I * (1 + 1 / 32)
+    fc1_flops = 2.0 * n_kept * 2 * I * H
+    layer_bytes = (D * H * I * 1.59375 + 2 * T * H + 4 * T * cfg.E + 2 * 1.03125 * T * H
+                   + 2 * 1.03125 * n_kept * I + 2 * T * H)
+    layer_flops = n_kept * 6.0 * H * I
+    prefill = args.workload in ("prefill_T8192",)
+    src = os.path.join(ROOT, "mxfp8_mxfp4_experts_amd", "csrc", "fc.hip")
+    traffic = _traffic(src, args.workload)
+    if prefill:
+        ach = fc1_flops / (fc1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_FP8_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    else:
+        ach = fc1_bytes / (fc1_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    roof.update({"kernel": "fc1_situ", "kernel_ms": round(fc1_ms, 5),
+                 "algorithmic_bytes": int(fc1_bytes), "algorithmic_flops": fc1_flops})
+
+    res = {
+        "metric": "MoE-layer tokens/s",
+        "value": round(T / (ms_per_step * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3xe2m1_f32acc",
+        "data": "synthetic (seeded; x~N(0,1) bf16, weights N(0,0.02) -> MXFP4)",
+        "config": {"workload": f"kimi_k3_moe_{args.workload}", "T": T, "H": H, "I": I,
+                   "E": cfg.E, "top_k": K, "E_local": E_local,
+                   "expert_offset": cfg.expert_offset, "experts_touched": D,
+                   "routed_rows": n_kept},
+        "layer": {"hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / 1e12
+                                     / MFMA_FP8_PEAK_TFLOPS, 4),
+                  "tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
+                  "gbs": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                  "wall_s_timed": round(wall, 3)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rid = idx.cpu().numpy()
+        rw = tw.cpu().numpy()
+        tps, threads, dt = cpu_baseline(cfg, act, w, rid, rw, n_tokens=1)
+        res["cpu_baseline"] = {"value": round(tps, 4), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"1 token of the same workload ({K} routes), "
+                                         f"{dt:.1f}s, oracle route-by-route float64"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * mi355moe.h -- C ABI of the MXFP8 x MXFP4 fused MoE expert layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (one GPU's share of a Kimi-K3-style routed-expert MoE) is five
+ * calls, issued in this order on one HIP stream:
+ *
+ *   moe_route        sigmoid + correction-bias top-k routing, renormalised weights
+ *   moe_quant_mxfp8  bf16 activations -> MXFP8 (E4M3 + one E8M0 scale per 32)
+ *   moe_permute      group the kept routes by local expert (stable)
+ *   moe_fc1_situ     grouped FC1 (MXFP8 x MXFP4) + SiTU + requantisation to MXFP8
+ *   moe_fc2_combine  grouped FC2 (MXFP8 x MXFP4) + top-k weighted combine to bf16
+ *
+ * Sources (the pages this library implements): page 1 = the SM120 FlashInfer
+ * MXFP4 experiment log for Kimi-K3 (sections "Serving call chain", "Key
+ * sources" table, "Real checkpoint contract", "TP/EP expert mapping", "Phase 2
+ * correctness harness", "NaN/Inf decision record"); page 5 = the Kimi-K3 MoE
+ * path notes (weight/scale layouts, symmetric buffer views, pre-dispatch
+ * quantisation).
+ *
+ * Conventions for every call:
+ *  - Every pointer is a DEVICE pointer owned by the caller.  The library never
+ *    allocates, frees or synchronises; every call is asynchronous on `stream`
+ *    (0 = the null stream) and keeps no state between calls.
+ *  - Arguments are validated before anything is launched.  A failed check
+ *    returns a status and launches nothing; the pure argument checks make no
+ *    HIP call, so they can be exercised on a machine without a GPU.  The
+ *    device check (gfx950) runs after them.  A launch failure returns
+ *    MOE_ERR_HIP.  Nothing retries or falls back to another path.
+ *  - Pointers to byte / bf16 tensors must be 16-byte aligned; float and int32
+ *    tensors 4-byte aligned.
+ *  - Shapes: H and I multiples of 128; 1 <= top_k <= min(E, 64); E <= 4096;
+ *    1 <= E_local <= 4096; T >= 1 (T = 0 is accepted and launches nothing).
+ *  - Byte layouts (little-endian, row-major):
+ *      E4M3  OCP 8-bit float "fn": bias 7, max 448, no infinities.
+ *      E2M1  4-bit float: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; two per byte,
+ *            element 2j in the low nibble of byte j (page 1: packed FP4,
+ *            two elements per byte; shapes [rows, K/2]).
+ *      E8M0  byte b is 2^(b-127); 0xFF is NaN (page 1, NaN/Inf record).
+ *    One scale per 32 consecutive elements along the contraction axis,
+ *    stored [rows, K/32] (page 1 checkpoint shapes; page 5 w13 scale
+ *    [E, 2I, H/32]).  The activation scale bytes [T, H/32] are the same bytes
+ *    as page 5's x_sf view [T, H/128] of int32 words.
+ */
+#ifndef MI355MOE_H
+#define MI355MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes have fixed values (page 1 records a Python/C++ enum mismatch
+ * that silently turned SiTU into a non-gated activation; these values never
+ * change within an ABI version). */
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,            /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,           /* a size or stride is out of range */
+  MOE_ERR_ALIGN = 3,           /* a pointer or stride is misaligned */
+  MOE_ERR_WORKSPACE = 5,       /* workspace too small */
+  MOE_ERR_HIP = 6,             /* a HIP runtime call or launch failed */
+  MOE_ERR_UNSUPPORTED_DEVICE = 7 /* current device is not gfx950 */
+} moe_status_t;
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* moe_strerror(int status);
+
+/* Bytes of workspace that moe_permute, moe_fc1_situ and moe_fc2_combine need
+ * for a layer call with these sizes (one buffer serves all three; moe_permute
+ * writes the FC kernels' tile schedule into it and moe_fc2_combine keeps the
+ * per-route FC2 rows there, so pass the same buffer to all three).
+ * Returns 0 for invalid sizes. */
+size_t moe_workspace_size(int T, int top_k, int E_local, int H, int I);
+
+/* a1 -- routing (page 1 "Serving call chain": sigmoid + correction bias +
+ * top-k + renormalise; "Key sources" routing row: the bias only selects, the
+ * weights come from the bias-free sigmoid scores, normalised; page 5: routed
+ * scaling factor).
+ *   logits  float [T, E], row stride ld_logits (>= E) elements.
+ *   bias    float [E] correction bias, or NULL for none.
+ *   s_e = float(sigmoid(logit) evaluated in double); key_e = s_e + bias_e in
+ *   float; the top_k largest keys, equal keys ranked by lower expert index,
+ *   slots ordered by key descending; w_k = s_k / sum_j s_j (double) times
+ *   routed_scaling, rounded to float.
+ *   topk_idx int32 [T, top_k] global expert ids; topk_w float [T, top_k].
+ *   Logits must be finite. */
+moe_status_t moe_route(const float* logits, int64_t ld_logits, const float* bias,
+                       int T, int E, int top_k, float routed_scaling,
+                       int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* a2 -- MXFP8 quantisation of bf16 activations (page 5 pre-dispatch step:
+ * absmax per 32 elements -> UE8M0 scale -> E4M3; page 1 NaN/Inf record:
+ * saturating finite conversion).
+ *   x   bf16 bits [T, H], row stride ld_x (>= H, multiple of 8) elements.
+ *   Per 32-element group: scale exponent e = the smallest integer with
+ *   absmax <= 448 * 2^e, clamped to [-127, 127] (0 for an all-zero group
+ *   gives e = -127); element = nearest E4M3 to x * 2^-e, ties to even,
+ *   saturating at +-448, sign of zero kept; NaN elements are ignored by the
+ *   absmax and encode as 0x00; a group holding +-Inf gets e = 127.
+ *   xq  uint8 E4M3 [T, H]; xs  uint8 E8M0 [T, H/32].  H % 32 == 0 suffices
+ *   for this call. */
+moe_status_t moe_quant_mxfp8(const uint16_t* x, int64_t ld_x, int T, int H,
+                             uint8_t* xq, uint8_t* xs, hipStream_t stream);
+
+/* a3 -- grouping by local expert (page 1 "TP/EP expert mapping": a GPU holds
+ * the contiguous experts [expert_offset, expert_offset + E_local) and maps
+ * global ids into that window; "Phase 2" coverage: -1 masked slots, empty
+ * experts).
+ *   topk_idx       int32 [T, top_k] global ids (-1 = masked slot).
+ *   Route r = t * top_k + k is kept iff its id lies in the window.
+ *   expert_offsets int32 [E_local + 1]: rows of local expert e are
+ *                  [expert_offsets[e], expert_offsets[e+1]).
+ *   sorted_route   int32 [T * top_k]: kept routes in grouped order, ascending
+ *                  r within an expert; entries past the kept count are -1.
+ *   route_row      int32 [T * top_k]: grouped row of route r, or -1 if dropped.
+ *   workspace      >= moe_workspace_size(...) bytes, 256-byte aligned; also
+ *                  receives the tile schedule read by the FC calls. */
+moe_status_t moe_permute(const int32_t* topk_idx, int T, int top_k, int expert_offset,
+                         int E_local, int32_t* expert_offsets, int32_t* sorted_route,
+                         int32_t* route_row, void* workspace, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* a4 + a5 + a6 -- FC1 grouped GEMM, SiTU, requantisation (page 1 "Serving call
+ * chain": grouped GEMM1 then gated activation; "Real checkpoint contract": w13
+ * holds [gate; up] in two contiguous halves, SiTU gate' = alpha *
+ * tanh(gate/alpha) * sigmoid(gate), up' = beta * tanh(up/beta), out = gate' *
+ * up' with alpha = 4, beta = 25; page 5: w13 [E, 2I, H/2], scales
+ * [E, 2I, H/32]).
+ *   xq, xs          MXFP8 activations from moe_quant_mxfp8 ([T, H], [T, H/32]).
+ *   expert_offsets, sorted_route   from moe_permute; grouped row j of expert e
+ *                   multiplies token sorted_route[j] / top_k.
+ *   w13, w13_s      uint8 [E_local, 2I, H/2], [E_local, 2I, H/32] (local window).
+ *   hq, hs          uint8 [T*top_k, I], [T*top_k, I/32]: the SiTU output of
+ *                   each kept grouped row, requantised with the moe_quant_mxfp8
+ *                   rule from the float accumulators (rows past the kept count
+ *                   are not written).
+ *   workspace       the buffer moe_permute filled. */
+moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
+                          int E_local, const int32_t* expert_offsets,
+                          const int32_t* sorted_route, const uint8_t* w13,
+                          const uint8_t* w13_s, float situ_alpha, float situ_beta,
+                          uint8_t* hq, uint8_t* hs, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* a7 + a8 -- FC2 grouped GEMM and top-k combine (page 1 "Serving call chain":
+ * GEMM2 then finalize; "Phase 2": non-fused finalize for bitwise determinism;
+ * page 5: w2 [E, H, I/2], scales [E, H, I/32]).
+ *   hq, hs          from moe_fc1_situ.
+ *   route_row       from moe_permute; topk_w from moe_route (float [T, top_k]).
+ *   w2, w2_s        uint8 [E_local, H, I/2], [E_local, H, I/32].
+ *   out             bf16 bits [T, H], row stride ld_out (>= H, multiple of 8):
+ *                   out[t] = bf16_rne( sum over kept k, in k order, of
+ *                   topk_w[t,k] * y[route_row[t,k]] ) with float accumulation;
+ *                   a token with no kept slot gets zeros.  Bitwise
+ *                   deterministic.
+ *   workspace       the buffer moe_permute filled (holds y [T*top_k, H] float). */
+moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
+                             int top_k, int E_local, const int32_t* expert_offsets,
+                             const int32_t* route_row, const float* topk_w,
+                             const uint8_t* w2, const uint8_t* w2_s, uint16_t* out,
+                             int64_t ld_out, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355MOE_H */

@@ -1,0 +1,20 @@
+"""MXFP8 x MXFP4 fused MoE expert layer for AMD Instinct MI355X (gfx950).
+
+The layer is five C calls into ``libmi355moe.so`` (declared in
+``include/mi355moe.h``); this package is their thin Python binding plus
+``MoELayer``, which issues the five calls in order with one workspace.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    MoEError,
+    lib,
+    load_library,
+    moe_abi_version,
+    moe_fc1_situ,
+    moe_fc2_combine,
+    moe_permute,
+    moe_quant_mxfp8,
+    moe_route,
+    moe_workspace_size,
+)
+from .layer import MoELayer  # noqa: F401

@@ -1,0 +1,82 @@
+// Shared device helpers and host-side layout of the MoE layer library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mi355moe {
+
+// ---------------------------------------------------------------------------
+// Limits checked at the C ABI.
+constexpr int kMaxExperts = 4096;   // routing width E and local window E_local
+constexpr int kMaxTopK = 64;        // one wavefront lane per selected slot
+constexpr int kGroup = 32;          // MX block: one E8M0 scale per 32 elements
+
+// FC tile heights (token rows per workgroup tile) for which moe_permute
+// writes a tile prefix: 16 << i for i in [0, kNumTileSizes).
+constexpr int kNumTileSizes = 4;
+
+// ---------------------------------------------------------------------------
+// Workspace layout shared by moe_permute / moe_fc1_situ / moe_fc2_combine.
+struct WsLayout {
+  size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1]
+  size_t y;             // float [T * top_k][H]  (FC2 rows before the combine)
+  size_t total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+inline WsLayout ws_layout(int T, int top_k, int E_local, int H) {
+  WsLayout l;
+  size_t off = 0;
+  l.tile_prefix = off;
+  off = align256(off + sizeof(int32_t) * kNumTileSizes * (size_t)(E_local + 1));
+  l.y = off;
+  off = align256(off + sizeof(float) * (size_t)T * top_k * H);
+  l.total = off;
+  return l;
+}
+
+// ---------------------------------------------------------------------------
+// Device helpers: the MX element / scale rules.
+
+// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127].  amax is a
+// non-negative float (NaN excluded by the caller).  448 = 1.75 * 2^8, so with
+// amax = 1.m * 2^p the rule is e = p - 8, plus one when 1.m > 1.75.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+  uint32_t b = __float_as_uint(amax);
+  uint32_t ex = b >> 23;            // sign is clear
+  if (ex == 0) return -127;         // zero or subnormal: 448 * 2^-127 > 2^-126
+  if (ex == 255) return 127;        // infinity
+  int e = (int)ex - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Nearest E4M3 code to y (ties to even), saturating at +-448, sign of zero
+// kept, NaN -> 0x00.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  uint32_t bits = __float_as_uint(y);
+  uint32_t sign = (bits >> 24) & 0x80u;
+  uint32_t ab = bits & 0x7FFFFFFFu;
+  if (ab > 0x7F800000u) return 0u;                     // NaN
+  uint32_t code;
+  if (ab < 0x3C800000u) {                              // |y| < 2^-6: subnormal grid m * 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(ab) * 512.0f);
+  } else {                                             // round 23 mantissa bits to 3 (RNE)
+    code = ((ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20) - (120u << 3);
+  }
+  code = code > 126u ? 126u : code;
+  return code | sign;
+}
+
+// float -> bf16 bits, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+}  // namespace mi355moe

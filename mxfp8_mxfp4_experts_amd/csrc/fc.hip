@@ -1,0 +1,331 @@
+// a4..a8: grouped FC1 (+ SiTU + requantisation) and FC2 (+ combine) on the
+// gfx950 block-scaled MFMA (V_MFMA_SCALE_F32_16X16X128_F8F6F4).
+//
+// Page 1, "Serving call chain": grouped GEMM1 -> gated activation -> GEMM2 ->
+// finalize; "Real checkpoint contract": w13 = [gate; up] halves, SiTU(4, 25);
+// page 5: w13 [E, 2I, H/2] + [E, 2I, H/32], w2 [E, H, I/2] + [E, H, I/32].
+//
+// MFMA operand layout (16x16x128, one wavefront; pinned by a one-hot probe of
+// the instruction): A = weights in E2M1 (cbsz 4), B = activations in E4M3
+// (blgp 0), out C[weight row][token].
+//   * lane l works on A row / B column l % 16; g = l / 16 is its lane group;
+//   * E2M1 operand: lane group g holds K [32g, 32g+32) as 16 bytes (low nibble
+//     first);
+//   * E4M3 operand: lane group g holds K [16g, 16g+16) in bytes 0..15 and
+//     K [64+16g, 64+16g+16) in bytes 16..31;
+//   * the scale byte of lane group b (selected by opsel) applies to
+//     K [32b, 32b+32) of that lane's row (A) or column (B);
+//   * C: lane l holds rows 4g .. 4g+3 of column l % 16.
+// So with K in natural order, MX block b of a 128-K slice is scaled by lane
+// group b on both operands.  Because a sum over K does not depend on its
+// order, one MFMA may take any four MX blocks as its slots provided both
+// operands agree: in a 512-K super-step, MFMA j gives slot b the block
+// 4b + j.  Each lane then streams 64 contiguous weight bytes and one scale
+// dword (byte j = opsel j) per super-step.
+//
+// Work decomposition: a workgroup (4 wavefronts) takes one tile of up to
+// 16*NT grouped rows of one expert and a column group of 4 units; a unit (one
+// wavefront) is 64 weight rows: for FC1, gate rows [c, c+32) with up rows
+// [I+c, I+c+32), so SiTU and the 32-column requantisation group are local to
+// the lanes that hold them; for FC2, output columns [h, h+64).
+#include "common.h"
+#include "launch.h"
+
+namespace mi355moe {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int J>
+__device__ __forceinline__ v4f mfma_w4a8(v4i w, v4i a_lo, v4i a_hi, v4f c, int ws, int as) {
+  v8i a8 = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+  v8i b8 = {a_lo[0], a_lo[1], a_lo[2], a_lo[3], a_hi[0], a_hi[1], a_hi[2], a_hi[3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 0, J, ws, J, as);
+}
+
+struct FcParams {
+  const uint8_t* act;        // FC1: xq [T, K]; FC2: hq [R, K]
+  const uint8_t* act_s;      // [.., K/32]
+  const int32_t* gather;     // FC1: sorted_route (grouped row -> route); FC2: unused
+  int top_k;
+  const uint8_t* w;          // [E_local, N, K/2]
+  const uint8_t* w_s;        // [E_local, N, K/32]
+  int K, N, I;
+  const int32_t* expert_offsets;
+  const int32_t* tile_prefix;  // [E_local + 1] for this kernel's tile height
+  int E_local;
+  int n_units, max_tiles;
+  float alpha, beta;
+  uint8_t* hq;               // FC1 out [R, I]
+  uint8_t* hs;               // FC1 out [R, I/32]
+  float* y;                  // FC2 out [R, N]
+};
+
+__device__ __forceinline__ float situ(float g, float u, float alpha, float beta) {
+  const float sig = 1.0f / (1.0f + __expf(-g));
+  return alpha * tanhf(g / alpha) * sig * (beta * tanhf(u / beta));
+}
+
+template <bool FC1, int NT>
+__global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
+  // Consecutive block ids land on different XCDs (round robin over 8); remap
+  // so that each XCD walks a contiguous range of (column group, tile) items,
+  // with the tiles of one expert adjacent and sharing its weights in L2.
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int logical = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  const int cg = logical / p.max_tiles, tile = logical % p.max_tiles;
+  const int* prefix = p.tile_prefix;
+  if (tile >= prefix[p.E_local]) return;
+  int lo = 0, hi = p.E_local;   // largest e with prefix[e] <= tile
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= tile) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int row_begin = p.expert_offsets[e] + (tile - prefix[e]) * (16 * NT);
+  const int row_end = min(p.expert_offsets[e + 1], row_begin + 16 * NT);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int u = cg * 4 + wave;
+  if (u >= p.n_units) return;
+  const int g = lane >> 4, li = lane & 15, h = g >> 1, ee = g & 1;
+  const int K = p.K;
+
+  int wrow[4];
+  if (FC1) {
+    const int c0 = u * 32;
+    wrow[0] = c0 + li; wrow[1] = c0 + 16 + li; wrow[2] = p.I + c0 + li; wrow[3] = p.I + c0 + 16 + li;
+  } else {
+    const int h0 = u * 64;
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) wrow[bk] = h0 + 16 * bk + li;
+  }
+  const uint8_t* wp[4];
+  const uint8_t* wsp[4];
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk) {
+    const size_t r = (size_t)e * p.N + wrow[bk];
+    wp[bk] = p.w + r * (K / 2);
+    wsp[bk] = p.w_s + r * (K / 32);
+  }
+  const uint8_t* ap[NT];
+  const uint8_t* asp[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    int row = min(row_begin + tt * 16 + li, row_end - 1);
+    size_t src = FC1 ? (size_t)(p.gather[row] / p.top_k) : (size_t)row;
+    ap[tt] = p.act + src * K;
+    asp[tt] = p.act_s + src * (K / 32);
+  }
+
+  v4f acc[NT][4];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) acc[tt][bk] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int n_super = K / 512;
+  for (int S = 0; S < n_super; ++S) {
+    v4i wv[4][4];
+    int wsv[4];
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      const uint8_t* src = wp[bk] + (size_t)(16 * S + 4 * g) * 16;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[bk][j] = *reinterpret_cast<const v4i*>(src + 16 * j);
+      wsv[bk] = *reinterpret_cast<const int*>(wsp[bk] + 16 * S + 4 * g);
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      v4i alo[4], ahi[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        alo[j] = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(16 * S + 4 * h + j) * 32 + 16 * ee);
+        ahi[j] = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(16 * S + 8 + 4 * h + j) * 32 + 16 * ee);
+      }
+      const int asv = *reinterpret_cast<const int*>(asp[tt] + 16 * S + 4 * g);
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk) {
+        acc[tt][bk] = mfma_w4a8<0>(wv[bk][0], alo[0], ahi[0], acc[tt][bk], wsv[bk], asv);
+        acc[tt][bk] = mfma_w4a8<1>(wv[bk][1], alo[1], ahi[1], acc[tt][bk], wsv[bk], asv);
+        acc[tt][bk] = mfma_w4a8<2>(wv[bk][2], alo[2], ahi[2], acc[tt][bk], wsv[bk], asv);
+        acc[tt][bk] = mfma_w4a8<3>(wv[bk][3], alo[3], ahi[3], acc[tt][bk], wsv[bk], asv);
+      }
+    }
+  }
+  // Remaining 128-K steps (K not a multiple of 512): slot b takes block 4s + b.
+  for (int s = n_super * 4; s < K / 128; ++s) {
+    v4i wv[4];
+    int wsv[4];
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      wv[bk] = *reinterpret_cast<const v4i*>(wp[bk] + (size_t)(4 * s + g) * 16);
+      wsv[bk] = wsp[bk][4 * s + g];
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      v4i alo = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(4 * s + h) * 32 + 16 * ee);
+      v4i ahi = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(4 * s + 2 + h) * 32 + 16 * ee);
+      const int asv = asp[tt][4 * s + g];
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk) acc[tt][bk] = mfma_w4a8<0>(wv[bk], alo, ahi, acc[tt][bk], wsv[bk], asv);
+    }
+  }
+
+  // The MFMAs read operands from all 64 lanes: make the accumulators live
+  // here, with every lane active, so no MFMA is moved into the per-lane
+  // store conditions below.
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(acc[tt][bk][r]));
+
+  // Epilogue.  Lane (g, li) holds rows 4g..4g+3 of each 16-row block for the
+  // token column li.
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const int row = row_begin + tt * 16 + li;
+    const bool valid = row < row_end;
+    if (FC1) {
+      const int c0 = u * 32;
+      float a[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        a[r] = situ(acc[tt][0][r], acc[tt][2][r], p.alpha, p.beta);       // column c0 + 4g + r
+        a[4 + r] = situ(acc[tt][1][r], acc[tt][3][r], p.alpha, p.beta);   // column c0 + 16 + 4g + r
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = fabsf(a[i]);
+        amax = v > amax ? v : amax;
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const int ex = mx8_exponent(amax);
+      uint32_t q0 = 0, q1 = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        q0 |= e4m3_encode(ldexpf(a[r], -ex)) << (8 * r);
+        q1 |= e4m3_encode(ldexpf(a[4 + r], -ex)) << (8 * r);
+      }
+      if (valid) {
+        uint8_t* dst = p.hq + (size_t)row * p.I + c0 + 4 * g;
+        *reinterpret_cast<uint32_t*>(dst) = q0;
+        *reinterpret_cast<uint32_t*>(dst + 16) = q1;
+        if (g == 0) p.hs[(size_t)row * (p.I / 32) + c0 / 32] = (uint8_t)(ex + 127);
+      }
+    } else {
+      if (valid) {
+        float* dst = p.y + (size_t)row * p.N + u * 64 + 4 * g;
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk)
+          *reinterpret_cast<v4f*>(dst + 16 * bk) = acc[tt][bk];
+      }
+    }
+  }
+}
+
+// out[t] = bf16( sum over kept k, in k order, of w[t,k] * y[route_row[t,k]] ).
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int H,
+                                                      const int32_t* __restrict__ route_row,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int K, uint16_t* __restrict__ out,
+                                                      int64_t ld_out) {
+  const int per_row = H / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * per_row) return;
+  const int t = (int)(gid / per_row), c = (int)(gid % per_row);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; ++k) {
+    const int rr = route_row[(size_t)t * K + k];
+    if (rr < 0) continue;
+    const float wk = topk_w[(size_t)t * K + k];
+    const v4f* src = reinterpret_cast<const v4f*>(y + (size_t)rr * H + (size_t)c * 8);
+    const v4f a = src[0], b2 = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] = fmaf(wk, a[i], acc[i]);
+      acc[4 + i] = fmaf(wk, b2[i], acc[4 + i]);
+    }
+  }
+  uint4 o;
+  o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+  o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+  o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+  o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * ld_out + (size_t)c * 8) = o;
+}
+
+int pick_nt(int R, int E_local) {
+  // Expected rows per touched expert decides the token-tile height.
+  const int touched = R < E_local ? R : E_local;
+  const int avg = touched > 0 ? R / touched : 1;
+  if (avg <= 24) return 1;
+  if (avg <= 48) return 2;
+  return 4;
+}
+
+template <bool FC1>
+hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, hipStream_t stream) {
+  const int nt = pick_nt(R, prm.E_local);
+  const int sel = nt == 1 ? 0 : (nt == 2 ? 1 : 2);
+  prm.tile_prefix = tile_prefix_all + (size_t)sel * (prm.E_local + 1);
+  const int tm = 16 * nt;
+  const int touched = R < prm.E_local ? R : prm.E_local;
+  prm.max_tiles = R / tm + touched;
+  const int groups = (prm.n_units + 3) / 4;
+  const int64_t blocks = (int64_t)groups * prm.max_tiles;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  switch (nt) {
+    case 1: hipLaunchKernelGGL((fc_kernel<FC1, 1>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
+    case 2: hipLaunchKernelGGL((fc_kernel<FC1, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
+    default: hipLaunchKernelGGL((fc_kernel<FC1, 4>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
+                      int E_local, const int32_t* offs, const int32_t* sorted_route,
+                      const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
+                      uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all,
+                      hipStream_t stream) {
+  FcParams p{};
+  p.act = xq; p.act_s = xs; p.gather = sorted_route; p.top_k = top_k;
+  p.w = w13; p.w_s = w13_s; p.K = H; p.N = 2 * I; p.I = I;
+  p.expert_offsets = offs; p.E_local = E_local;
+  p.n_units = I / 32;
+  p.alpha = alpha; p.beta = beta; p.hq = hq; p.hs = hs; p.y = nullptr;
+  return launch_fc<true>(p, T * top_k, tile_prefix_all, stream);
+}
+
+hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
+                      int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
+                      float* y, const int32_t* tile_prefix_all, hipStream_t stream) {
+  FcParams p{};
+  p.act = hq; p.act_s = hs; p.gather = nullptr; p.top_k = top_k;
+  p.w = w2; p.w_s = w2_s; p.K = I; p.N = H; p.I = I;
+  p.expert_offsets = offs; p.E_local = E_local;
+  p.n_units = H / 64;
+  p.y = y;
+  return launch_fc<false>(p, T * top_k, tile_prefix_all, stream);
+}
+
+hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,
+                          int T, int K, uint16_t* out, int64_t ld_out, hipStream_t stream) {
+  const int64_t threads = (int64_t)T * (H / 8);
+  const int blocks = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, y, H, route_row, topk_w,
+                     T, K, out, ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace mi355moe

@@ -1,0 +1,27 @@
+// Kernel launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355moe {
+
+hipError_t launch_route(const float* logits, int64_t ld, const float* bias, int T, int E, int K,
+                        float scaling, int32_t* idx, float* w, hipStream_t stream);
+hipError_t launch_quant(const uint16_t* x, int64_t ld, int T, int H, uint8_t* xq, uint8_t* xs,
+                        hipStream_t stream);
+hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, int32_t* offs,
+                          int32_t* sorted_route, int32_t* route_row, int32_t* tile_prefix,
+                          hipStream_t stream);
+hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
+                      int E_local, const int32_t* offs, const int32_t* sorted_route,
+                      const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
+                      uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all,
+                      hipStream_t stream);
+hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
+                      int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
+                      float* y, const int32_t* tile_prefix_all, hipStream_t stream);
+hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,
+                          int T, int K, uint16_t* out, int64_t ld_out, hipStream_t stream);
+
+}  // namespace mi355moe

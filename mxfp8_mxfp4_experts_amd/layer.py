@@ -1,0 +1,71 @@
+"""``MoELayer``: the five C calls of the expert layer, in order, on one stream.
+
+Buffers (routing outputs, MXFP8 activations, grouping, FC1 output and the
+workspace) are allocated once for ``max_tokens`` and reused, so a call
+allocates nothing but its output (or nothing when ``out`` is given).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+class MoELayer:
+    def __init__(self, w13, w13_s, w2, w2_s, *, top_k: int, E: int, expert_offset: int = 0,
+                 routed_scaling: float = 1.0, situ_alpha: float = 4.0, situ_beta: float = 25.0,
+                 max_tokens: int = 1):
+        for name, t in (("w13", w13), ("w13_s", w13_s), ("w2", w2), ("w2_s", w2_s)):
+            B._need(t, name, torch.uint8)
+        self.E_local, twoI, half_h = w13.shape
+        self.H, self.I = 2 * half_h, twoI // 2
+        self.w13, self.w13_s, self.w2, self.w2_s = w13, w13_s, w2, w2_s
+        self.top_k, self.E, self.expert_offset = top_k, E, expert_offset
+        self.routed_scaling, self.alpha, self.beta = routed_scaling, situ_alpha, situ_beta
+        self.device = w13.device
+        self._alloc(max_tokens)
+
+    def _alloc(self, T: int):
+        dev, K, H, I = self.device, self.top_k, self.H, self.I
+        R = T * K
+        self.max_tokens = T
+        self.topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        self.xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+        self.expert_offsets = torch.empty(self.E_local + 1, dtype=torch.int32, device=dev)
+        self.sorted_route = torch.empty(R, dtype=torch.int32, device=dev)
+        self.route_row = torch.empty(R, dtype=torch.int32, device=dev)
+        self.hq = torch.empty((R, I), dtype=torch.uint8, device=dev)
+        self.hs = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+        n = B.moe_workspace_size(T, K, self.E_local, H, I)
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def __call__(self, x: torch.Tensor, logits: torch.Tensor, bias: Optional[torch.Tensor],
+                 out: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                 topk_w: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """x bf16 [T, H]; logits float [T, E]; bias float [E] or None.
+
+        ``topk_idx``/``topk_w`` (int32 / float [T, top_k]) replace the routing
+        step when given (e.g. masked -1 slots)."""
+        T = x.shape[0]
+        if T > self.max_tokens:
+            self._alloc(T)
+        K = self.top_k
+        idx, w = self.topk_idx[:T], self.topk_w[:T]
+        if topk_idx is None:
+            B.moe_route(logits, bias, K, self.routed_scaling, idx, w)
+        else:
+            idx, w = topk_idx, topk_w
+        xq, xs = B.moe_quant_mxfp8(x, self.xq[:T], self.xs[:T])
+        R = T * K
+        B.moe_permute(idx, self.expert_offset, self.E_local, self.workspace, self.expert_offsets,
+                      self.sorted_route[:R], self.route_row[:R])
+        B.moe_fc1_situ(xq, xs, K, self.expert_offsets, self.sorted_route[:R], self.w13,
+                       self.w13_s, self.workspace, self.alpha, self.beta, self.hq[:R],
+                       self.hs[:R])
+        return B.moe_fc2_combine(self.hq[:R], self.hs[:R], T, K, self.expert_offsets,
+                                 self.route_row[:R], w, self.w2, self.w2_s, self.workspace,
+                                 out)

@@ -122,7 +122,7 @@ def situ(g, u, alpha: float = 4.0, beta: float = 25.0):
 # a4 + a5 + a6: FC1, SiTU, requantisation
 # --------------------------------------------------------------------------
 def fc1_situ_requant(xq, xs, expert_offsets, sorted_route, top_k, w13, w13_s,
-                     alpha=4.0, beta=25.0, return_acc=False):
+                     alpha=4.0, beta=25.0, return_acc=False, return_pre=False):
     """Per local expert: gather its routed rows of the MXFP8 activations,
     multiply by the dequantised MXFP4 w13 (exact in float64), split the
     result into the gate half (columns < I) and the up half (columns >= I),
@@ -135,7 +135,8 @@ def fc1_situ_requant(xq, xs, expert_offsets, sorted_route, top_k, w13, w13_s,
     activations (the FC2 activation scale slot); the SiTU output is not
     rounded before it.  Rows are in grouped order.
     Returns (hq uint8 [n_kept, I], hs uint8 [n_kept, I/32]) and, with
-    ``return_acc``, the float64 FC1 accumulators [n_kept, 2I].
+    ``return_acc``, the float64 FC1 accumulators [n_kept, 2I]; with
+    ``return_pre``, the float64 SiTU output before requantisation.
     """
     w13 = np.asarray(w13)
     E_local, twoI, _ = w13.shape
@@ -155,9 +156,8 @@ def fc1_situ_requant(xq, xs, expert_offsets, sorted_route, top_k, w13, w13_s,
             acc_all[r0:r1] = acc
         a_all[r0:r1] = situ(acc[:, :I], acc[:, I:], alpha, beta)
     hq, hs = mxfp8_quantize(a_all) if n_kept else (np.zeros((0, I), np.uint8), np.zeros((0, I // 32), np.uint8))
-    if return_acc:
-        return hq, hs, acc_all
-    return hq, hs
+    extra = ([acc_all] if return_acc else []) + ([a_all] if return_pre else [])
+    return (hq, hs, *extra) if extra else (hq, hs)
 
 
 # --------------------------------------------------------------------------
@@ -219,11 +219,12 @@ def oracle_layer(x_bf16, logits, bias, w13, w13_s, w2, w2_s, *, top_k,
         topk_idx, topk_w = route(logits, bias, top_k, routed_scaling)
     xq, xs = quant_x(x_bf16)
     offs, sroute, rrow = permute(topk_idx, expert_offset, E_local)
-    hq, hs = fc1_situ_requant(xq, xs, offs, sroute, top_k, w13, w13_s, alpha, beta)
+    hq, hs, a = fc1_situ_requant(xq, xs, offs, sroute, top_k, w13, w13_s, alpha, beta,
+                                 return_pre=True)
     y = fc2(hq, hs, offs, w2, w2_s)
     out = combine(y, rrow, topk_w, T, top_k)
     return dict(topk_idx=topk_idx, topk_w=topk_w, xq=xq, xs=xs, expert_offsets=offs,
-                sorted_route=sroute, route_row=rrow, hq=hq, hs=hs, y=y, out=out)
+                sorted_route=sroute, route_row=rrow, hq=hq, hs=hs, a=a, y=y, out=out)
 
 
 def oracle_tokens(tokens, x_bf16, topk_idx, topk_w, weight_fn, *, top_k, expert_offset,
@@ -235,7 +236,8 @@ def oracle_tokens(tokens, x_bf16, topk_idx, topk_w, weight_fn, *, top_k, expert_
     and quantisation are per token, FC1/FC2 per route), so the result equals
     the corresponding rows of ``oracle_layer``.  ``weight_fn(e_local)``
     returns (w13[e], w13_s[e], w2[e], w2_s[e]) as numpy arrays.
-    Returns dict(out [n,H] float64, hq/hs per (token, slot)).
+    Returns dict(out [n,H] float64, h {(j, k): (hq, hs, SiTU output before
+    requantisation)} for sampled token j and slot k).
     """
     tokens = list(tokens)
     xq, xs = quant_x(np.asarray(x_bf16)[tokens])
@@ -263,7 +265,7 @@ def oracle_tokens(tokens, x_bf16, topk_idx, topk_w, weight_fn, *, top_k, expert_
         y = mxfp8_dequantize(hq, hs) @ W2.T
         for i, (j, k) in enumerate(need[e]):
             ys[(j, k)] = y[i]
-            hqs[(j, k)] = (hq[i], hs[i])
+            hqs[(j, k)] = (hq[i], hs[i], a[i])
     for j, t in enumerate(tokens):
         for k in range(top_k):
             if (j, k) in ys:

@@ -1,0 +1,126 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355moe.h")
+LIB = os.path.join(ROOT, "mxfp8_mxfp4_experts_amd", "libmi355moe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmi355moe.so not built")
+
+
+def _header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+\**)+(moe_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mxfp8_mxfp4_experts_amd import _binding
+    return _binding.load_library(LIB)
+
+
+def test_header_declares_expected_calls():
+    syms = _header_symbols()
+    for name in ("moe_route", "moe_quant_mxfp8", "moe_permute", "moe_fc1_situ",
+                 "moe_fc2_combine", "moe_workspace_size", "moe_strerror", "moe_abi_version"):
+        assert name in syms
+
+
+def test_library_exports_every_header_symbol(lib):
+    from mxfp8_mxfp4_experts_amd._binding import EXPORTS
+    raw = ctypes.CDLL(LIB)
+    for name in _header_symbols():
+        assert hasattr(raw, name), name
+    assert set(_header_symbols()) == set(EXPORTS)
+
+
+def test_version_and_strerror(lib):
+    assert lib.moe_abi_version() == 1
+    for code in (0, 1, 2, 3, 5, 6, 7):
+        assert lib.moe_strerror(code)
+    assert lib.moe_strerror(99) == b"unknown status"
+
+
+def test_workspace_size(lib):
+    n = lib.moe_workspace_size(8, 16, 896, 7168, 3584)
+    # tile prefix + y rows [T*K, H] float
+    assert n >= 8 * 16 * 7168 * 4 and n % 256 == 0
+    assert lib.moe_workspace_size(8, 16, 896, 7000, 3584) == 0      # H % 128
+    assert lib.moe_workspace_size(8, 0, 896, 7168, 3584) == 0       # top_k
+    assert lib.moe_workspace_size(8, 16, 5000, 7168, 3584) == 0     # E_local
+
+
+FAKE = 1 << 20          # 16-byte aligned, never dereferenced by a failing call
+MIS = FAKE + 2          # misaligned
+
+
+def test_route_validation(lib):
+    st = lib.moe_route
+    assert st(FAKE, 4, FAKE, 5, 4, 0, 1.0, FAKE, FAKE, None) == 2          # top_k 0
+    assert st(FAKE, 4, FAKE, 5, 4, 5, 1.0, FAKE, FAKE, None) == 2          # top_k > E
+    assert st(FAKE, 3, FAKE, 5, 4, 2, 1.0, FAKE, FAKE, None) == 2          # ld < E
+    assert st(FAKE, 5000, None, 5, 5000, 2, 1.0, FAKE, FAKE, None) == 2    # E > 4096
+    assert st(None, 4, FAKE, 5, 4, 2, 1.0, FAKE, FAKE, None) == 1          # null logits
+    assert st(FAKE, 4, FAKE, 5, 4, 2, 1.0, None, FAKE, None) == 1
+    assert st(MIS, 4, FAKE, 5, 4, 2, 1.0, FAKE, FAKE, None) == 3
+    assert st(None, 4, None, 0, 4, 2, 1.0, None, None, None) == 0          # T = 0: nothing
+
+
+def test_quant_validation(lib):
+    q = lib.moe_quant_mxfp8
+    assert q(FAKE, 128, 4, 100, FAKE, FAKE, None) == 2                     # H % 32
+    assert q(FAKE, 64, 4, 128, FAKE, FAKE, None) == 2                      # ld < H
+    assert q(None, 128, 4, 128, FAKE, FAKE, None) == 1
+    assert q(FAKE + 8, 128, 4, 128, FAKE, FAKE, None) == 3                 # x not 16-aligned
+    assert q(FAKE, 132, 4, 128, FAKE, FAKE, None) == 3                     # ld % 8
+
+
+def test_permute_validation(lib):
+    p = lib.moe_permute
+    assert p(FAKE, 4, 0, 0, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2   # top_k
+    assert p(FAKE, 4, 2, -1, 8, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2  # offset
+    assert p(FAKE, 4, 2, 0, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == 2   # E_local
+    assert p(FAKE, 4, 2, 0, 8, None, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert p(FAKE, 4, 2, 0, 8, FAKE, FAKE, FAKE, FAKE + 16, 1 << 20, None) == 3  # ws align
+    assert p(FAKE, 4, 2, 0, 8, FAKE, FAKE, FAKE, FAKE, 8, None) == 5          # ws too small
+
+
+def test_fc_validation(lib):
+    f1 = lib.moe_fc1_situ
+    args = [FAKE, FAKE, 4, 256, 128, 2, 4, FAKE, FAKE, FAKE, FAKE, 4.0, 25.0, FAKE, FAKE, FAKE,
+            1 << 30, None]
+    bad = list(args); bad[3] = 200
+    assert f1(*bad) == 2                                                    # H % 128
+    bad = list(args); bad[11] = 0.0
+    assert f1(*bad) == 2                                                    # alpha
+    bad = list(args); bad[9] = None
+    assert f1(*bad) == 1                                                    # w13 null
+    bad = list(args); bad[9] = MIS
+    assert f1(*bad) == 3
+    bad = list(args); bad[16] = 16
+    assert f1(*bad) == 5
+    f2 = lib.moe_fc2_combine
+    args2 = [FAKE, FAKE, 4, 256, 128, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE,
+             1 << 30, None]
+    bad = list(args2); bad[13] = 128
+    assert f2(*bad) == 2                                                    # ld_out < H
+    bad = list(args2); bad[13] = 260
+    assert f2(*bad) == 3                                                    # ld_out % 8
+    bad = list(args2); bad[15] = 1024
+    assert f2(*bad) == 5
+    bad = list(args2); bad[12] = None
+    assert f2(*bad) == 1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    from mxfp8_mxfp4_experts_amd import _binding as B
+    with pytest.raises(ValueError):
+        B.moe_route(torch.zeros(4, 8), None, 2)
+    with pytest.raises(ValueError):
+        B.moe_quant_mxfp8(torch.zeros(4, 128, dtype=torch.bfloat16))
