@@ -17,11 +17,8 @@
 //     K [32b, 32b+32) of that lane's row (A) or column (B);
 //   * C: lane l holds rows 4g .. 4g+3 of column l % 16.
 // So with K in natural order, MX block b of a 128-K slice is scaled by lane
-// group b on both operands.  Because a sum over K does not depend on its
-// order, one MFMA may take any four MX blocks as its slots provided both
-// operands agree: in a 512-K super-step, MFMA j gives slot b the block
-// 4b + j.  Each lane then streams 64 contiguous weight bytes and one scale
-// dword (byte j = opsel j) per super-step.
+// group b on both operands, and each weight-load instruction reads 64
+// contiguous bytes of each of 16 rows.
 //
 // Work decomposition: a workgroup (4 wavefronts) takes one tile of up to
 // 16*NT grouped rows of one expert and a column group of 4 units; a unit (one
@@ -69,6 +66,55 @@ __device__ __forceinline__ float situ(float g, float u, float alpha, float beta)
   return alpha * tanhf(g / alpha) * sig * (beta * tanhf(u / beta));
 }
 
+// Operands of one 512-K super-step for one wavefront.
+template <int NT>
+struct Stage {
+  v4i w[4][4];      // [row block][MFMA j]: 32 E2M1 weights of this lane
+  v4i ws[4];        // [row block]: the row's 16 scale bytes of the super-step
+  v4i alo[NT][4];   // [token tile][MFMA j]: E4M3 K [16g, 16g+16) of the slice
+  v4i ahi[NT][4];   //                      E4M3 K [64+16g, 64+16g+16)
+  v4i as[NT];       // the token's 16 scale bytes
+};
+
+template <int NT>
+__device__ __forceinline__ void load_stage(Stage<NT>& st, const uint8_t* const* wp,
+                                           const uint8_t* const* wsp, const uint8_t* const* ap,
+                                           const uint8_t* const* asp, int S, int g) {
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk) {
+    const v4i* src = reinterpret_cast<const v4i*>(wp[bk] + (size_t)S * 256 + 16 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.w[bk][j] = __builtin_nontemporal_load(src + 4 * j);
+    st.ws[bk] = *reinterpret_cast<const v4i*>(wsp[bk] + (size_t)S * 16);
+  }
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const uint8_t* a = ap[tt] + (size_t)S * 512 + 16 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st.alo[tt][j] = *reinterpret_cast<const v4i*>(a + 128 * j);
+      st.ahi[tt][j] = *reinterpret_cast<const v4i*>(a + 128 * j + 64);
+    }
+    st.as[tt] = *reinterpret_cast<const v4i*>(asp[tt] + (size_t)S * 16);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void compute_stage(v4f (&acc)[NT][4], const Stage<NT>& st, int g) {
+  const int sh = 8 * g;
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int asv = st.as[tt][j] >> sh;
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk)
+        acc[tt][bk] = mfma_w4a8<0>(st.w[bk][j], st.alo[tt][j], st.ahi[tt][j], acc[tt][bk],
+                                   st.ws[bk][j] >> sh, asv);
+    }
+  }
+}
+
 template <bool FC1, int NT>
 __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   // Consecutive block ids land on different XCDs (round robin over 8); remap
@@ -91,7 +137,7 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int u = cg * 4 + wave;
   if (u >= p.n_units) return;
-  const int g = lane >> 4, li = lane & 15, h = g >> 1, ee = g & 1;
+  const int g = lane >> 4, li = lane & 15;
   const int K = p.K;
 
   int wrow[4];
@@ -127,35 +173,30 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) acc[tt][bk] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // Super-steps of 512 K: MFMA j takes the 128-K slice [512S + 128j, +128) in
+  // natural order, so slot b holds MX block 16S + 4j + b.  Both operands'
+  // scales for the super-step are one 16-byte chunk per row; lane group g
+  // uses byte 4j + g of it (a shift by 8g of dword j).  The next super-step's
+  // operands are loaded before this one's MFMAs are issued (two register
+  // stages), keeping a wavefront's weight stream in flight.
   const int n_super = K / 512;
-  for (int S = 0; S < n_super; ++S) {
-    v4i wv[4][4];
-    int wsv[4];
-#pragma unroll
-    for (int bk = 0; bk < 4; ++bk) {
-      const uint8_t* src = wp[bk] + (size_t)(16 * S + 4 * g) * 16;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) wv[bk][j] = *reinterpret_cast<const v4i*>(src + 16 * j);
-      wsv[bk] = *reinterpret_cast<const int*>(wsp[bk] + 16 * S + 4 * g);
-    }
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-      v4i alo[4], ahi[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        alo[j] = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(16 * S + 4 * h + j) * 32 + 16 * ee);
-        ahi[j] = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(16 * S + 8 + 4 * h + j) * 32 + 16 * ee);
-      }
-      const int asv = *reinterpret_cast<const int*>(asp[tt] + 16 * S + 4 * g);
-#pragma unroll
-      for (int bk = 0; bk < 4; ++bk) {
-        acc[tt][bk] = mfma_w4a8<0>(wv[bk][0], alo[0], ahi[0], acc[tt][bk], wsv[bk], asv);
-        acc[tt][bk] = mfma_w4a8<1>(wv[bk][1], alo[1], ahi[1], acc[tt][bk], wsv[bk], asv);
-        acc[tt][bk] = mfma_w4a8<2>(wv[bk][2], alo[2], ahi[2], acc[tt][bk], wsv[bk], asv);
-        acc[tt][bk] = mfma_w4a8<3>(wv[bk][3], alo[3], ahi[3], acc[tt][bk], wsv[bk], asv);
-      }
-    }
+  Stage<NT> st0, st1;
+  // No branch inside the loop: the wait-count pass then lets the stage just
+  // loaded stay in flight while the other stage's MFMAs issue.  When n_super
+  // is even the last iteration reloads the final stage (an L2 hit).
+  if (n_super > 0) load_stage<NT>(st0, wp, wsp, ap, asp, 0, g);
+  int S = 0;
+  for (; S + 1 < n_super; S += 2) {
+    load_stage<NT>(st1, wp, wsp, ap, asp, S + 1, g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<NT>(acc, st0, g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage<NT>(st0, wp, wsp, ap, asp, min(S + 2, n_super - 1), g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<NT>(acc, st1, g);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (S < n_super) compute_stage<NT>(acc, st0, g);
   // Remaining 128-K steps (K not a multiple of 512): slot b takes block 4s + b.
   for (int s = n_super * 4; s < K / 128; ++s) {
     v4i wv[4];
@@ -167,8 +208,8 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
-      v4i alo = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(4 * s + h) * 32 + 16 * ee);
-      v4i ahi = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)(4 * s + 2 + h) * 32 + 16 * ee);
+      v4i alo = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)s * 128 + 16 * g);
+      v4i ahi = *reinterpret_cast<const v4i*>(ap[tt] + (size_t)s * 128 + 64 + 16 * g);
       const int asv = asp[tt][4 * s + g];
 #pragma unroll
       for (int bk = 0; bk < 4; ++bk) acc[tt][bk] = mfma_w4a8<0>(wv[bk], alo, ahi, acc[tt][bk], wsv[bk], asv);
@@ -266,15 +307,13 @@ int pick_nt(int R, int E_local) {
   // Expected rows per touched expert decides the token-tile height.
   const int touched = R < E_local ? R : E_local;
   const int avg = touched > 0 ? R / touched : 1;
-  if (avg <= 24) return 1;
-  if (avg <= 48) return 2;
-  return 4;
+  return avg <= 24 ? 1 : 2;
 }
 
 template <bool FC1>
 hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, hipStream_t stream) {
   const int nt = pick_nt(R, prm.E_local);
-  const int sel = nt == 1 ? 0 : (nt == 2 ? 1 : 2);
+  const int sel = nt == 1 ? 0 : 1;
   prm.tile_prefix = tile_prefix_all + (size_t)sel * (prm.E_local + 1);
   const int tm = 16 * nt;
   const int touched = R < prm.E_local ? R : prm.E_local;
@@ -285,8 +324,7 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, hipStr
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   switch (nt) {
     case 1: hipLaunchKernelGGL((fc_kernel<FC1, 1>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
-    case 2: hipLaunchKernelGGL((fc_kernel<FC1, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
-    default: hipLaunchKernelGGL((fc_kernel<FC1, 4>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
+    default: hipLaunchKernelGGL((fc_kernel<FC1, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
   }
   return hipGetLastError();
 }
