@@ -17,10 +17,12 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// 0 = unknown, 1 = gfx950, 2 = other.  A cache of a fixed device property.
+// Per device: 0 = unknown, 1 = gfx950, 2 = other; and its compute-unit count.
+// A cache of fixed device properties.
 std::atomic<int> g_device_ok[256];
+std::atomic<int> g_device_cus[256];
 
-moe_status_t check_device() {
+moe_status_t check_device(int* n_cu = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
   if (dev < 0 || dev >= 256) return MOE_ERR_UNSUPPORTED_DEVICE;
@@ -28,9 +30,11 @@ moe_status_t check_device() {
   if (s == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_HIP;
+    g_device_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     g_device_ok[dev].store(s, std::memory_order_relaxed);
   }
+  if (n_cu) *n_cu = g_device_cus[dev].load(std::memory_order_relaxed);
   return s == 1 ? MOE_OK : MOE_ERR_UNSUPPORTED_DEVICE;
 }
 
@@ -148,12 +152,13 @@ moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, in
   WsLayout l = ws_layout(T, top_k, E_local, H);
   if (ws_bytes < l.y) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
-  moe_status_t s = check_device();
+  int n_cu = 0;
+  moe_status_t s = check_device(&n_cu);
   if (s != MOE_OK) return s;
   const int32_t* prefix =
       reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + l.tile_prefix);
   return finish(launch_fc1(xq, xs, T, H, I, top_k, E_local, expert_offsets, sorted_route, w13,
-                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, stream));
+                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, n_cu, stream));
 }
 
 moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
@@ -175,13 +180,14 @@ moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H,
   WsLayout l = ws_layout(T, top_k, E_local, H);
   if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
-  moe_status_t s = check_device();
+  int n_cu = 0;
+  moe_status_t s = check_device(&n_cu);
   if (s != MOE_OK) return s;
   char* ws = static_cast<char*>(workspace);
   const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + l.tile_prefix);
   float* y = reinterpret_cast<float*>(ws + l.y);
   hipError_t e = launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, prefix,
-                            stream);
+                            n_cu, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return finish(launch_combine(y, H, route_row, topk_w, T, top_k, out, ld_out, stream));
 }

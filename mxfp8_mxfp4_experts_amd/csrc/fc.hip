@@ -26,45 +26,12 @@
 // [I+c, I+c+32), so SiTU and the 32-column requantisation group are local to
 // the lanes that hold them; for FC2, output columns [h, h+64).
 #include "common.h"
+#include "fc_common.h"
 #include "launch.h"
 
 namespace mi355moe {
 
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-template <int J>
-__device__ __forceinline__ v4f mfma_w4a8(v4i w, v4i a_lo, v4i a_hi, v4f c, int ws, int as) {
-  v8i a8 = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
-  v8i b8 = {a_lo[0], a_lo[1], a_lo[2], a_lo[3], a_hi[0], a_hi[1], a_hi[2], a_hi[3]};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, c, 4, 0, J, ws, J, as);
-}
-
-struct FcParams {
-  const uint8_t* act;        // FC1: xq [T, K]; FC2: hq [R, K]
-  const uint8_t* act_s;      // [.., K/32]
-  const int32_t* gather;     // FC1: sorted_route (grouped row -> route); FC2: unused
-  int top_k;
-  const uint8_t* w;          // [E_local, N, K/2]
-  const uint8_t* w_s;        // [E_local, N, K/32]
-  int K, N, I;
-  const int32_t* expert_offsets;
-  const int32_t* tile_prefix;  // [E_local + 1] for this kernel's tile height
-  int E_local;
-  int n_units, max_tiles;
-  float alpha, beta;
-  uint8_t* hq;               // FC1 out [R, I]
-  uint8_t* hs;               // FC1 out [R, I/32]
-  float* y;                  // FC2 out [R, N]
-};
-
-__device__ __forceinline__ float situ(float g, float u, float alpha, float beta) {
-  const float sig = 1.0f / (1.0f + __expf(-g));
-  return alpha * tanhf(g / alpha) * sig * (beta * tanhf(u / beta));
-}
 
 // Operands of one 512-K super-step for one wavefront.
 template <int NT>
@@ -125,12 +92,7 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   const int cg = logical / p.max_tiles, tile = logical % p.max_tiles;
   const int* prefix = p.tile_prefix;
   if (tile >= prefix[p.E_local]) return;
-  int lo = 0, hi = p.E_local;   // largest e with prefix[e] <= tile
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= tile) lo = mid; else hi = mid;
-  }
-  const int e = lo;
+  const int e = find_expert(prefix, p.E_local, tile);
   const int row_begin = p.expert_offsets[e] + (tile - prefix[e]) * (16 * NT);
   const int row_end = min(p.expert_offsets[e + 1], row_begin + 16 * NT);
 
@@ -220,55 +182,12 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   // here, with every lane active, so no MFMA is moved into the per-lane
   // store conditions below.
 #pragma unroll
-  for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-    for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(acc[tt][bk][r]));
+  for (int tt = 0; tt < NT; ++tt) pin_acc(acc[tt]);
 
-  // Epilogue.  Lane (g, li) holds rows 4g..4g+3 of each 16-row block for the
-  // token column li.
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
     const int row = row_begin + tt * 16 + li;
-    const bool valid = row < row_end;
-    if (FC1) {
-      const int c0 = u * 32;
-      float a[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        a[r] = situ(acc[tt][0][r], acc[tt][2][r], p.alpha, p.beta);       // column c0 + 4g + r
-        a[4 + r] = situ(acc[tt][1][r], acc[tt][3][r], p.alpha, p.beta);   // column c0 + 16 + 4g + r
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float v = fabsf(a[i]);
-        amax = v > amax ? v : amax;
-      }
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      const int ex = mx8_exponent(amax);
-      uint32_t q0 = 0, q1 = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        q0 |= e4m3_encode(ldexpf(a[r], -ex)) << (8 * r);
-        q1 |= e4m3_encode(ldexpf(a[4 + r], -ex)) << (8 * r);
-      }
-      if (valid) {
-        uint8_t* dst = p.hq + (size_t)row * p.I + c0 + 4 * g;
-        *reinterpret_cast<uint32_t*>(dst) = q0;
-        *reinterpret_cast<uint32_t*>(dst + 16) = q1;
-        if (g == 0) p.hs[(size_t)row * (p.I / 32) + c0 / 32] = (uint8_t)(ex + 127);
-      }
-    } else {
-      if (valid) {
-        float* dst = p.y + (size_t)row * p.N + u * 64 + 4 * g;
-#pragma unroll
-        for (int bk = 0; bk < 4; ++bk)
-          *reinterpret_cast<v4f*>(dst + 16 * bk) = acc[tt][bk];
-      }
-    }
+    store_subtile<FC1>(p, acc[tt], row, row < row_end, u, g);
   }
 }
 
@@ -303,18 +222,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint4*>(out + (size_t)t * ld_out + (size_t)c * 8) = o;
 }
 
-int pick_nt(int R, int E_local) {
-  // Expected rows per touched expert decides the token-tile height.
+int expected_rows(int R, int E_local) {
   const int touched = R < E_local ? R : E_local;
-  const int avg = touched > 0 ? R / touched : 1;
-  return avg <= 24 ? 1 : 2;
+  return touched > 0 ? R / touched : 1;
 }
 
 template <bool FC1>
-hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, hipStream_t stream) {
-  const int nt = pick_nt(R, prm.E_local);
-  const int sel = nt == 1 ? 0 : 1;
-  prm.tile_prefix = tile_prefix_all + (size_t)sel * (prm.E_local + 1);
+hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_cu,
+                     hipStream_t stream) {
+  const int avg = expected_rows(R, prm.E_local);
+  if (avg >= 32 && prefill_shape_ok(prm.K, FC1 ? prm.I : prm.N, FC1)) {
+    // Tile height 128 (prefix index 3); one 512-thread workgroup per CU.
+    prm.tile_prefix = tile_prefix_all + (size_t)3 * (prm.E_local + 1);
+    const int n_wg = (n_cu > 8 ? n_cu : 8) & ~7;
+    return launch_fc_prefill(FC1, prm, n_wg, stream);
+  }
+  const int nt = avg <= 24 ? 1 : 2;
+  prm.tile_prefix = tile_prefix_all + (size_t)(nt == 1 ? 0 : 1) * (prm.E_local + 1);
   const int tm = 16 * nt;
   const int touched = R < prm.E_local ? R : prm.E_local;
   prm.max_tiles = R / tm + touched;
@@ -322,10 +246,10 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, hipStr
   const int64_t blocks = (int64_t)groups * prm.max_tiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  switch (nt) {
-    case 1: hipLaunchKernelGGL((fc_kernel<FC1, 1>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
-    default: hipLaunchKernelGGL((fc_kernel<FC1, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, prm); break;
-  }
+  if (nt == 1)
+    hipLaunchKernelGGL((fc_kernel<FC1, 1>), dim3((unsigned)blocks), dim3(256), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((fc_kernel<FC1, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -334,7 +258,7 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, hipStr
 hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
-                      uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all,
+                      uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all, int n_cu,
                       hipStream_t stream) {
   FcParams p{};
   p.act = xq; p.act_s = xs; p.gather = sorted_route; p.top_k = top_k;
@@ -342,19 +266,19 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = I / 32;
   p.alpha = alpha; p.beta = beta; p.hq = hq; p.hs = hs; p.y = nullptr;
-  return launch_fc<true>(p, T * top_k, tile_prefix_all, stream);
+  return launch_fc<true>(p, T * top_k, tile_prefix_all, n_cu, stream);
 }
 
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      float* y, const int32_t* tile_prefix_all, hipStream_t stream) {
+                      float* y, const int32_t* tile_prefix_all, int n_cu, hipStream_t stream) {
   FcParams p{};
   p.act = hq; p.act_s = hs; p.gather = nullptr; p.top_k = top_k;
   p.w = w2; p.w_s = w2_s; p.K = I; p.N = H; p.I = I;
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = H / 64;
   p.y = y;
-  return launch_fc<false>(p, T * top_k, tile_prefix_all, stream);
+  return launch_fc<false>(p, T * top_k, tile_prefix_all, n_cu, stream);
 }
 
 hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,

@@ -105,6 +105,10 @@ MID_SHAPES = [
     # many experts, few rows each (decode-like tiles)
     dict(T=5, H=1024, I=512, E=64, K=8),
     dict(T=64, H=384, I=256, E=32, K=2, bias_kind="zero"),
+    # many rows per expert: the LDS-tiled prefill kernels (K % 256 == 0), with
+    # experts spanning several 128-row tiles plus a partial last tile
+    dict(T=600, H=1024, I=512, E=8, K=2),
+    dict(T=700, H=768, I=256, E=32, K=4, E_local=8, expert_offset=16),
 ]
 
 
