@@ -30,7 +30,8 @@
  *  - Pointers to byte / bf16 tensors must be 16-byte aligned; float and int32
  *    tensors 4-byte aligned.
  *  - Shapes: H and I multiples of 128; 1 <= top_k <= min(E, 64); E <= 4096;
- *    1 <= E_local <= 4096; T >= 1 (T = 0 is accepted and launches nothing).
+ *    1 <= E_local <= 4096; T >= 0 (with T = 0 nothing is launched, except
+ *    that moe_permute still writes zero expert offsets).
  *  - Byte layouts (little-endian, row-major):
  *      E4M3  OCP 8-bit float "fn": bias 7, max 448, no infinities.
  *      E2M1  4-bit float: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; two per byte,
@@ -169,6 +170,55 @@ moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H,
                              const uint8_t* w2, const uint8_t* w2_s, uint16_t* out,
                              int64_t ld_out, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Tiled weight layout (optional, one-time).  The calls above read the
+ * checkpoint layout directly.  moe_prepack_w13 / moe_prepack_w2 reorder the
+ * same bytes once, at load time, into a tiled layout whose blocks the FC
+ * kernels read as whole contiguous pieces; moe_fc1_situ_tiled /
+ * moe_fc2_combine_tiled then compute exactly what moe_fc1_situ /
+ * moe_fc2_combine compute (this is the role of the weight and scale
+ * transforms the pages apply after loading, page 5).
+ *
+ * Tiled layout, for a weight matrix of N rows and K columns per expert
+ * (w13: N = 2I, K = H; w2: N = H, K = I): rows are grouped 512 at a time
+ * (group cg) and K is cut into stages of 128.  Block (e, cg, s) holds
+ *   data   32768 bytes: 16-byte chunk number (4w + i) * 64 + l is the logical
+ *          16-byte chunk c = (l & 3) ^ ((l >> 3) & 3) of stage s of row
+ *          r = 64w + 16i + l/4 (w < 8, i < 4, l < 64);
+ *   scales 2048 bytes: dword r = the four scale bytes of row r for MX blocks
+ *          4s .. 4s+3;
+ * where group row r is global row: w13 — unit u = 8cg + r/64, b = (r/16) % 4,
+ * row = (b < 2 ? 0 : I) + 32u + 16(b % 2) + r % 16 (gate rows of the unit,
+ * then the matching up rows); w2 — 512cg + r.  Blocks are stored in
+ * [e][cg][s] order; the tiled data and scale arrays have the sizes of the
+ * checkpoint arrays.  Requires I % 256 == 0 (w13) and H % 512 == 0 (w2).
+ * ------------------------------------------------------------------------- */
+
+/* Reorder checkpoint w13 [E_local, 2I, H/2] + w13_s [E_local, 2I, H/32] into
+ * w13t / w13t_s (same sizes, distinct buffers).  Asynchronous on `stream`. */
+moe_status_t moe_prepack_w13(const uint8_t* w13, const uint8_t* w13_s, int E_local, int H, int I,
+                             uint8_t* w13t, uint8_t* w13t_s, hipStream_t stream);
+
+/* Reorder checkpoint w2 [E_local, H, I/2] + w2_s [E_local, H, I/32]. */
+moe_status_t moe_prepack_w2(const uint8_t* w2, const uint8_t* w2_s, int E_local, int H, int I,
+                            uint8_t* w2t, uint8_t* w2t_s, hipStream_t stream);
+
+/* moe_fc1_situ on tiled w13 (from moe_prepack_w13); same results. */
+moe_status_t moe_fc1_situ_tiled(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
+                                int top_k, int E_local, const int32_t* expert_offsets,
+                                const int32_t* sorted_route, const uint8_t* w13t,
+                                const uint8_t* w13t_s, float situ_alpha, float situ_beta,
+                                uint8_t* hq, uint8_t* hs, void* workspace, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* moe_fc2_combine on tiled w2 (from moe_prepack_w2); same results. */
+moe_status_t moe_fc2_combine_tiled(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
+                                   int top_k, int E_local, const int32_t* expert_offsets,
+                                   const int32_t* route_row, const float* topk_w,
+                                   const uint8_t* w2t, const uint8_t* w2t_s, uint16_t* out,
+                                   int64_t ld_out, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,8 @@ from ._binding import (  # noqa: F401
     moe_fc1_situ,
     moe_fc2_combine,
     moe_permute,
+    moe_prepack_w13,
+    moe_prepack_w2,
     moe_quant_mxfp8,
     moe_route,
     moe_workspace_size,

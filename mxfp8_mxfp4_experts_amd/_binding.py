@@ -25,7 +25,8 @@ MOE_STATUS = {
 # Entry points declared in include/mi355moe.h.
 EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_route", "moe_quant_mxfp8",
-    "moe_permute", "moe_fc1_situ", "moe_fc2_combine",
+    "moe_permute", "moe_fc1_situ", "moe_fc2_combine", "moe_prepack_w13", "moe_prepack_w2",
+    "moe_fc1_situ_tiled", "moe_fc2_combine_tiled",
 )
 
 _P = ctypes.c_void_p
@@ -59,6 +60,13 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.moe_fc2_combine.restype = _I
     lib.moe_fc2_combine.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P,
                                     _SZ, _P]
+    lib.moe_fc1_situ_tiled.restype = _I
+    lib.moe_fc1_situ_tiled.argtypes = lib.moe_fc1_situ.argtypes
+    lib.moe_fc2_combine_tiled.restype = _I
+    lib.moe_fc2_combine_tiled.argtypes = lib.moe_fc2_combine.argtypes
+    for name in ("moe_prepack_w13", "moe_prepack_w2"):
+        getattr(lib, name).restype = _I
+        getattr(lib, name).argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
     return lib
 
 
@@ -192,7 +200,10 @@ def moe_permute(topk_idx: torch.Tensor, expert_offset: int, E_local: int, worksp
 
 
 def moe_fc1_situ(xq, xs, top_k, expert_offsets, sorted_route, w13, w13_s, workspace,
-                 situ_alpha: float = 4.0, situ_beta: float = 25.0, hq=None, hs=None):
+                 situ_alpha: float = 4.0, situ_beta: float = 25.0, hq=None, hs=None,
+                 tiled: bool = False):
+    """``tiled``: w13 / w13_s come from ``moe_prepack_w13`` (calls
+    moe_fc1_situ_tiled); they keep the checkpoint tensor shapes."""
     _need(xq, "xq", torch.uint8)
     T, H = xq.shape
     dev = xq.device
@@ -213,7 +224,8 @@ def moe_fc1_situ(xq, xs, top_k, expert_offsets, sorted_route, w13, w13_s, worksp
         hs = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
     _need(hq, "hq", torch.uint8, (R, I), device=dev)
     _need(hs, "hs", torch.uint8, (R, I // 32), device=dev)
-    _check("moe_fc1_situ", lib().moe_fc1_situ(
+    name = "moe_fc1_situ_tiled" if tiled else "moe_fc1_situ"
+    _check(name, getattr(lib(), name)(
         _ptr(xq), _ptr(xs), T, H, I, top_k, E_local, _ptr(expert_offsets), _ptr(sorted_route),
         _ptr(w13), _ptr(w13_s), float(situ_alpha), float(situ_beta), _ptr(hq), _ptr(hs),
         _ptr(workspace), workspace.numel(), _stream()))
@@ -221,7 +233,9 @@ def moe_fc1_situ(xq, xs, top_k, expert_offsets, sorted_route, w13, w13_s, worksp
 
 
 def moe_fc2_combine(hq, hs, T, top_k, expert_offsets, route_row, topk_w, w2, w2_s, workspace,
-                    out=None):
+                    out=None, tiled: bool = False):
+    """``tiled``: w2 / w2_s come from ``moe_prepack_w2`` (calls
+    moe_fc2_combine_tiled)."""
     _need(hq, "hq", torch.uint8)
     R, I = hq.shape
     dev = hq.device
@@ -243,8 +257,31 @@ def moe_fc2_combine(hq, hs, T, top_k, expert_offsets, route_row, topk_w, w2, w2_
         raise ValueError("out must be [T, H] with unit column stride")
     ob = _as_u16(out, "out")
     _need(ob, "out", torch.uint16, contiguous=False, device=dev)
-    _check("moe_fc2_combine", lib().moe_fc2_combine(
+    name = "moe_fc2_combine_tiled" if tiled else "moe_fc2_combine"
+    _check(name, getattr(lib(), name)(
         _ptr(hq), _ptr(hs), T, H, I, top_k, E_local, _ptr(expert_offsets), _ptr(route_row),
         _ptr(topk_w), _ptr(w2), _ptr(w2_s), _ptr(ob), out.stride(0), _ptr(workspace),
         workspace.numel(), _stream()))
     return out
+
+
+def _prepack(name, w, w_s, H, I):
+    _need(w, name + " weights", torch.uint8)
+    _need(w_s, name + " scales", torch.uint8, device=w.device)
+    tw = torch.empty_like(w)
+    tws = torch.empty_like(w_s)
+    _check(name, getattr(lib(), name)(_ptr(w), _ptr(w_s), w.shape[0], H, I, _ptr(tw), _ptr(tws),
+                                      _stream()))
+    return tw, tws
+
+
+def moe_prepack_w13(w13, w13_s):
+    """Checkpoint w13 [E, 2I, H/2] + scales -> tiled copies (same shapes)."""
+    E, twoI, half_h = w13.shape
+    return _prepack("moe_prepack_w13", w13, w13_s, 2 * half_h, twoI // 2)
+
+
+def moe_prepack_w2(w2, w2_s):
+    """Checkpoint w2 [E, H, I/2] + scales -> tiled copies (same shapes)."""
+    E, H, half_i = w2.shape
+    return _prepack("moe_prepack_w2", w2, w2_s, H, 2 * half_i)

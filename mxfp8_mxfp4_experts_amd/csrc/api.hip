@@ -133,12 +133,13 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int top_k, int expert_o
                                sorted_route, route_row, prefix, stream));
 }
 
-moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
+static moe_status_t fc1_impl(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
                           int E_local, const int32_t* expert_offsets,
                           const int32_t* sorted_route, const uint8_t* w13,
                           const uint8_t* w13_s, float situ_alpha, float situ_beta, uint8_t* hq,
-                          uint8_t* hs, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (!valid_hi(H, I) || !valid_window(top_k, E_local) || !valid_rows(T, top_k, H, I))
+                          uint8_t* hs, void* workspace, size_t ws_bytes, hipStream_t stream,
+                          bool tiled) {
+  if (!valid_hi(H, I) || (tiled && I % 256 != 0) || !valid_window(top_k, E_local) || !valid_rows(T, top_k, H, I))
     return MOE_ERR_SHAPE;
   if (!(situ_alpha > 0.0f) || !(situ_beta > 0.0f)) return MOE_ERR_SHAPE;
   if (!expert_offsets || !w13 || !w13_s || !workspace) return MOE_ERR_NULL;
@@ -158,16 +159,35 @@ moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, in
   const int32_t* prefix =
       reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + l.tile_prefix);
   return finish(launch_fc1(xq, xs, T, H, I, top_k, E_local, expert_offsets, sorted_route, w13,
-                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, n_cu, stream));
+                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, n_cu, tiled, stream));
 }
 
-moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
+moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
+                          int E_local, const int32_t* expert_offsets,
+                          const int32_t* sorted_route, const uint8_t* w13,
+                          const uint8_t* w13_s, float situ_alpha, float situ_beta, uint8_t* hq,
+                          uint8_t* hs, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return fc1_impl(xq, xs, T, H, I, top_k, E_local, expert_offsets, sorted_route, w13, w13_s,
+                  situ_alpha, situ_beta, hq, hs, workspace, ws_bytes, stream, false);
+}
+
+moe_status_t moe_fc1_situ_tiled(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
+                                int top_k, int E_local, const int32_t* expert_offsets,
+                                const int32_t* sorted_route, const uint8_t* w13t,
+                                const uint8_t* w13t_s, float situ_alpha, float situ_beta,
+                                uint8_t* hq, uint8_t* hs, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  return fc1_impl(xq, xs, T, H, I, top_k, E_local, expert_offsets, sorted_route, w13t, w13t_s,
+                  situ_alpha, situ_beta, hq, hs, workspace, ws_bytes, stream, true);
+}
+
+static moe_status_t fc2_impl(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                              int top_k, int E_local, const int32_t* expert_offsets,
                              const int32_t* route_row, const float* topk_w, const uint8_t* w2,
                              const uint8_t* w2_s, uint16_t* out, int64_t ld_out,
-                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+                             void* workspace, size_t ws_bytes, hipStream_t stream, bool tiled) {
   if (!valid_hi(H, I) || !valid_window(top_k, E_local) || !valid_rows(T, top_k, H, I) ||
-      ld_out < H)
+      ld_out < H || (tiled && H % 512 != 0))
     return MOE_ERR_SHAPE;
   if (!expert_offsets || !w2 || !w2_s || !workspace) return MOE_ERR_NULL;
   if (T > 0 && (!hq || !hs || !route_row || !topk_w || !out)) return MOE_ERR_NULL;
@@ -187,9 +207,51 @@ moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H,
   const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + l.tile_prefix);
   float* y = reinterpret_cast<float*>(ws + l.y);
   hipError_t e = launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, prefix,
-                            n_cu, stream);
+                            n_cu, tiled, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return finish(launch_combine(y, H, route_row, topk_w, T, top_k, out, ld_out, stream));
+}
+
+moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
+                             int top_k, int E_local, const int32_t* expert_offsets,
+                             const int32_t* route_row, const float* topk_w, const uint8_t* w2,
+                             const uint8_t* w2_s, uint16_t* out, int64_t ld_out,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return fc2_impl(hq, hs, T, H, I, top_k, E_local, expert_offsets, route_row, topk_w, w2, w2_s,
+                  out, ld_out, workspace, ws_bytes, stream, false);
+}
+
+moe_status_t moe_fc2_combine_tiled(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
+                                   int top_k, int E_local, const int32_t* expert_offsets,
+                                   const int32_t* route_row, const float* topk_w,
+                                   const uint8_t* w2t, const uint8_t* w2t_s, uint16_t* out,
+                                   int64_t ld_out, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return fc2_impl(hq, hs, T, H, I, top_k, E_local, expert_offsets, route_row, topk_w, w2t, w2t_s,
+                  out, ld_out, workspace, ws_bytes, stream, true);
+}
+
+static moe_status_t prepack_impl(bool fc1, const uint8_t* w, const uint8_t* ws, int E_local,
+                                 int H, int I, uint8_t* tw, uint8_t* tws, hipStream_t stream) {
+  if (!valid_hi(H, I) || E_local < 1 || E_local > kMaxExperts) return MOE_ERR_SHAPE;
+  if (fc1 ? (I % 256 != 0) : (H % 512 != 0)) return MOE_ERR_SHAPE;
+  if (!w || !ws || !tw || !tws) return MOE_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(ws, 16) || !aligned(tw, 16) || !aligned(tws, 16))
+    return MOE_ERR_ALIGN;
+  moe_status_t s = check_device();
+  if (s != MOE_OK) return s;
+  const int N = fc1 ? 2 * I : H, K = fc1 ? H : I;
+  return finish(launch_prepack(fc1, w, ws, E_local, N, K, I, tw, tws, stream));
+}
+
+moe_status_t moe_prepack_w13(const uint8_t* w13, const uint8_t* w13_s, int E_local, int H, int I,
+                             uint8_t* w13t, uint8_t* w13t_s, hipStream_t stream) {
+  return prepack_impl(true, w13, w13_s, E_local, H, I, w13t, w13t_s, stream);
+}
+
+moe_status_t moe_prepack_w2(const uint8_t* w2, const uint8_t* w2_s, int E_local, int H, int I,
+                            uint8_t* w2t, uint8_t* w2t_s, hipStream_t stream) {
+  return prepack_impl(false, w2, w2_s, E_local, H, I, w2t, w2t_s, stream);
 }
 
 }  // extern "C"

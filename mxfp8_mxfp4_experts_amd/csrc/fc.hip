@@ -28,6 +28,7 @@
 #include "common.h"
 #include "fc_common.h"
 #include "launch.h"
+#include "tiled.h"
 
 namespace mi355moe {
 
@@ -38,21 +39,35 @@ template <int NT>
 struct Stage {
   v4i w[4][4];      // [row block][MFMA j]: 32 E2M1 weights of this lane
   v4i ws[4];        // [row block]: the row's 16 scale bytes of the super-step
+                    // (dword j = MX blocks 16S + 4j .. 16S + 4j + 3)
   v4i alo[NT][4];   // [token tile][MFMA j]: E4M3 K [16g, 16g+16) of the slice
   v4i ahi[NT][4];   //                      E4M3 K [64+16g, 64+16g+16)
   v4i as[NT];       // the token's 16 scale bytes
 };
 
-template <int NT>
+// Checkpoint layout: wp[bk] points at the lane's row + 16g, wsp[bk] at the
+// row's scale bytes.  Tiled layout: wp[bk] points at the lane's 16 bytes in
+// stage 0's block and wsp[bk] at the row's scale dword there; stage t adds t
+// whole blocks.
+template <int NT, bool TILED>
 __device__ __forceinline__ void load_stage(Stage<NT>& st, const uint8_t* const* wp,
                                            const uint8_t* const* wsp, const uint8_t* const* ap,
                                            const uint8_t* const* asp, int S, int g) {
 #pragma unroll
   for (int bk = 0; bk < 4; ++bk) {
-    const v4i* src = reinterpret_cast<const v4i*>(wp[bk] + (size_t)S * 256 + 16 * g);
+    if (TILED) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.w[bk][j] = __builtin_nontemporal_load(src + 4 * j);
-    st.ws[bk] = *reinterpret_cast<const v4i*>(wsp[bk] + (size_t)S * 16);
+      for (int j = 0; j < 4; ++j) {
+        st.w[bk][j] = __builtin_nontemporal_load(
+            reinterpret_cast<const v4i*>(wp[bk] + (size_t)(4 * S + j) * kTileBytes));
+        st.ws[bk][j] = *reinterpret_cast<const int*>(wsp[bk] + (size_t)(4 * S + j) * kTileScaleBytes);
+      }
+    } else {
+      const v4i* src = reinterpret_cast<const v4i*>(wp[bk] + (size_t)S * 256);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.w[bk][j] = __builtin_nontemporal_load(src + 4 * j);
+      st.ws[bk] = *reinterpret_cast<const v4i*>(wsp[bk] + (size_t)S * 16);
+    }
   }
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
@@ -82,7 +97,7 @@ __device__ __forceinline__ void compute_stage(v4f (&acc)[NT][4], const Stage<NT>
   }
 }
 
-template <bool FC1, int NT>
+template <bool FC1, int NT, bool TILED>
 __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   // Consecutive block ids land on different XCDs (round robin over 8); remap
   // so that each XCD walks a contiguous range of (column group, tile) items,
@@ -113,11 +128,24 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   }
   const uint8_t* wp[4];
   const uint8_t* wsp[4];
+  if (TILED) {
+    // Unit u is rows [64 (u % 8), +64) of column group u / 8; block bk is its
+    // 1 KB chunk 4 (u % 8) + bk, where row li's logical chunk g sits at
+    // position 4 li + (g ^ ((li >> 1) & 3)).
+    const int tcg = u >> 3, wu = u & 7;
+    const size_t blk0 = tiled_block(e, tcg, 0, p.N / kTileRows, K / kTileK);
 #pragma unroll
-  for (int bk = 0; bk < 4; ++bk) {
-    const size_t r = (size_t)e * p.N + wrow[bk];
-    wp[bk] = p.w + r * (K / 2);
-    wsp[bk] = p.w_s + r * (K / 32);
+    for (int bk = 0; bk < 4; ++bk) {
+      wp[bk] = p.w + blk0 * kTileBytes + (4 * wu + bk) * 1024 + 16 * (4 * li + (g ^ ((li >> 1) & 3)));
+      wsp[bk] = p.w_s + blk0 * kTileScaleBytes + (64 * wu + 16 * bk + li) * 4;
+    }
+  } else {
+#pragma unroll
+    for (int bk = 0; bk < 4; ++bk) {
+      const size_t r = (size_t)e * p.N + wrow[bk];
+      wp[bk] = p.w + r * (K / 2) + 16 * g;
+      wsp[bk] = p.w_s + r * (K / 32);
+    }
   }
   const uint8_t* ap[NT];
   const uint8_t* asp[NT];
@@ -146,14 +174,14 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   // No branch inside the loop: the wait-count pass then lets the stage just
   // loaded stay in flight while the other stage's MFMAs issue.  When n_super
   // is even the last iteration reloads the final stage (an L2 hit).
-  if (n_super > 0) load_stage<NT>(st0, wp, wsp, ap, asp, 0, g);
+  if (n_super > 0) load_stage<NT, TILED>(st0, wp, wsp, ap, asp, 0, g);
   int S = 0;
   for (; S + 1 < n_super; S += 2) {
-    load_stage<NT>(st1, wp, wsp, ap, asp, S + 1, g);
+    load_stage<NT, TILED>(st1, wp, wsp, ap, asp, S + 1, g);
     __builtin_amdgcn_sched_barrier(0);
     compute_stage<NT>(acc, st0, g);
     __builtin_amdgcn_sched_barrier(0);
-    load_stage<NT>(st0, wp, wsp, ap, asp, min(S + 2, n_super - 1), g);
+    load_stage<NT, TILED>(st0, wp, wsp, ap, asp, min(S + 2, n_super - 1), g);
     __builtin_amdgcn_sched_barrier(0);
     compute_stage<NT>(acc, st1, g);
     __builtin_amdgcn_sched_barrier(0);
@@ -165,8 +193,13 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
     int wsv[4];
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) {
-      wv[bk] = *reinterpret_cast<const v4i*>(wp[bk] + (size_t)(4 * s + g) * 16);
-      wsv[bk] = wsp[bk][4 * s + g];
+      if (TILED) {
+        wv[bk] = *reinterpret_cast<const v4i*>(wp[bk] + (size_t)s * kTileBytes);
+        wsv[bk] = *reinterpret_cast<const int*>(wsp[bk] + (size_t)s * kTileScaleBytes) >> (8 * g);
+      } else {
+        wv[bk] = *reinterpret_cast<const v4i*>(wp[bk] + (size_t)s * 64);
+        wsv[bk] = wsp[bk][4 * s + g];
+      }
     }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
@@ -228,14 +261,14 @@ int expected_rows(int R, int E_local) {
 }
 
 template <bool FC1>
-hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_cu,
+hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_cu, bool tiled,
                      hipStream_t stream) {
   const int avg = expected_rows(R, prm.E_local);
-  if (avg >= 32 && prefill_shape_ok(prm.K, FC1 ? prm.I : prm.N, FC1)) {
+  if (avg >= 32 && prefill_shape_ok(prm, FC1)) {
     // Tile height 128 (prefix index 3); one 512-thread workgroup per CU.
     prm.tile_prefix = tile_prefix_all + (size_t)3 * (prm.E_local + 1);
     const int n_wg = (n_cu > 8 ? n_cu : 8) & ~7;
-    return launch_fc_prefill(FC1, prm, n_wg, stream);
+    return launch_fc_prefill(FC1, tiled, prm, n_wg, stream);
   }
   const int nt = avg <= 24 ? 1 : 2;
   prm.tile_prefix = tile_prefix_all + (size_t)(nt == 1 ? 0 : 1) * (prm.E_local + 1);
@@ -246,10 +279,14 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_
   const int64_t blocks = (int64_t)groups * prm.max_tiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (nt == 1)
-    hipLaunchKernelGGL((fc_kernel<FC1, 1>), dim3((unsigned)blocks), dim3(256), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((fc_kernel<FC1, 2>), dim3((unsigned)blocks), dim3(256), 0, stream, prm);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (tiled) {
+    if (nt == 1) hipLaunchKernelGGL((fc_kernel<FC1, 1, true>), grid, block, 0, stream, prm);
+    else hipLaunchKernelGGL((fc_kernel<FC1, 2, true>), grid, block, 0, stream, prm);
+  } else {
+    if (nt == 1) hipLaunchKernelGGL((fc_kernel<FC1, 1, false>), grid, block, 0, stream, prm);
+    else hipLaunchKernelGGL((fc_kernel<FC1, 2, false>), grid, block, 0, stream, prm);
+  }
   return hipGetLastError();
 }
 
@@ -259,26 +296,27 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
                       uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all, int n_cu,
-                      hipStream_t stream) {
+                      bool tiled, hipStream_t stream) {
   FcParams p{};
-  p.act = xq; p.act_s = xs; p.gather = sorted_route; p.top_k = top_k;
+  p.act = xq; p.act_s = xs; p.act_rows = T; p.gather = sorted_route; p.top_k = top_k;
   p.w = w13; p.w_s = w13_s; p.K = H; p.N = 2 * I; p.I = I;
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = I / 32;
   p.alpha = alpha; p.beta = beta; p.hq = hq; p.hs = hs; p.y = nullptr;
-  return launch_fc<true>(p, T * top_k, tile_prefix_all, n_cu, stream);
+  return launch_fc<true>(p, T * top_k, tile_prefix_all, n_cu, tiled, stream);
 }
 
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      float* y, const int32_t* tile_prefix_all, int n_cu, hipStream_t stream) {
+                      float* y, const int32_t* tile_prefix_all, int n_cu, bool tiled,
+                      hipStream_t stream) {
   FcParams p{};
-  p.act = hq; p.act_s = hs; p.gather = nullptr; p.top_k = top_k;
+  p.act = hq; p.act_s = hs; p.act_rows = (int64_t)T * top_k; p.gather = nullptr; p.top_k = top_k;
   p.w = w2; p.w_s = w2_s; p.K = I; p.N = H; p.I = I;
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = H / 64;
   p.y = y;
-  return launch_fc<false>(p, T * top_k, tile_prefix_all, n_cu, stream);
+  return launch_fc<false>(p, T * top_k, tile_prefix_all, n_cu, tiled, stream);
 }
 
 hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,

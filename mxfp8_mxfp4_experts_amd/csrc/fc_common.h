@@ -21,6 +21,7 @@ __device__ __forceinline__ v4f mfma_w4a8(v4i w, v4i a_lo, v4i a_hi, v4f c, int w
 struct FcParams {
   const uint8_t* act;        // FC1: xq [T, K]; FC2: hq [R, K]
   const uint8_t* act_s;      // [.., K/32]
+  int64_t act_rows;          // rows of act: FC1 T, FC2 R
   const int32_t* gather;     // FC1: sorted_route (grouped row -> route); FC2: unused
   int top_k;
   const uint8_t* w;          // [E_local, N, K/2]

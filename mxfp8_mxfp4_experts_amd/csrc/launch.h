@@ -17,15 +17,21 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
                       uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all, int n_cu,
-                      hipStream_t stream);
+                      bool tiled, hipStream_t stream);
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      float* y, const int32_t* tile_prefix_all, int n_cu, hipStream_t stream);
+                      float* y, const int32_t* tile_prefix_all, int n_cu, bool tiled,
+                      hipStream_t stream);
 struct FcParams;
-// Prefill-shaped FC kernels (fc_prefill.hip): usable when K % 256 == 0 and the
-// output columns split into 256-row weight tiles.
-bool prefill_shape_ok(int K, int N_cols, bool fc1);
-hipError_t launch_fc_prefill(bool fc1, const FcParams& prm, int n_wg, hipStream_t stream);
+// Prefill-shaped FC kernels (fc_prefill.hip): usable when K % 128 == 0, the
+// output columns split into 512-row weight tiles and the operands fit 32-bit
+// buffer offsets.
+bool prefill_shape_ok(const FcParams& prm, bool fc1);
+hipError_t launch_fc_prefill(bool fc1, bool tiled, const FcParams& prm, int n_wg,
+                             hipStream_t stream);
+// One-time reordering of checkpoint-layout weights into the tiled layout.
+hipError_t launch_prepack(bool fc1, const uint8_t* w, const uint8_t* ws, int E_local, int N,
+                          int K, int I, uint8_t* tw, uint8_t* tws, hipStream_t stream);
 hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,
                           int T, int K, uint16_t* out, int64_t ld_out, hipStream_t stream);
 

@@ -3,6 +3,10 @@
 Buffers (routing outputs, MXFP8 activations, grouping, FC1 output and the
 workspace) are allocated once for ``max_tokens`` and reused, so a call
 allocates nothing but its output (or nothing when ``out`` is given).
+
+With ``tiled=True`` (the default where the shapes allow it: I % 256 == 0 and
+H % 512 == 0) the weights are reordered once into the library's tiled layout
+at construction and the tiled FC entry points are used; results are the same.
 """
 from __future__ import annotations
 
@@ -16,11 +20,17 @@ from . import _binding as B
 class MoELayer:
     def __init__(self, w13, w13_s, w2, w2_s, *, top_k: int, E: int, expert_offset: int = 0,
                  routed_scaling: float = 1.0, situ_alpha: float = 4.0, situ_beta: float = 25.0,
-                 max_tokens: int = 1):
+                 max_tokens: int = 1, tiled: Optional[bool] = None):
         for name, t in (("w13", w13), ("w13_s", w13_s), ("w2", w2), ("w2_s", w2_s)):
             B._need(t, name, torch.uint8)
         self.E_local, twoI, half_h = w13.shape
         self.H, self.I = 2 * half_h, twoI // 2
+        if tiled is None:
+            tiled = self.I % 256 == 0 and self.H % 512 == 0
+        self.tiled = tiled
+        if tiled:
+            w13, w13_s = B.moe_prepack_w13(w13, w13_s)
+            w2, w2_s = B.moe_prepack_w2(w2, w2_s)
         self.w13, self.w13_s, self.w2, self.w2_s = w13, w13_s, w2, w2_s
         self.top_k, self.E, self.expert_offset = top_k, E, expert_offset
         self.routed_scaling, self.alpha, self.beta = routed_scaling, situ_alpha, situ_beta
@@ -65,7 +75,7 @@ class MoELayer:
                       self.sorted_route[:R], self.route_row[:R])
         B.moe_fc1_situ(xq, xs, K, self.expert_offsets, self.sorted_route[:R], self.w13,
                        self.w13_s, self.workspace, self.alpha, self.beta, self.hq[:R],
-                       self.hs[:R])
+                       self.hs[:R], tiled=self.tiled)
         return B.moe_fc2_combine(self.hq[:R], self.hs[:R], T, K, self.expert_offsets,
                                  self.route_row[:R], w, self.w2, self.w2_s, self.workspace,
-                                 out)
+                                 out, tiled=self.tiled)

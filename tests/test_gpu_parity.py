@@ -34,11 +34,11 @@ def _lib():
     return m
 
 
-def _layer_for(cfg, w, max_tokens):
+def _layer_for(cfg, w, max_tokens, tiled=None):
     m = _lib()
     return m.MoELayer(w["w13"], w["w13_s"], w["w2"], w["w2_s"], top_k=cfg.K, E=cfg.E,
                       expert_offset=cfg.expert_offset, routed_scaling=cfg.routed_scaling,
-                      max_tokens=max_tokens)
+                      max_tokens=max_tokens, tiled=tiled)
 
 
 def _device_inputs(act):
@@ -116,11 +116,55 @@ MID_SHAPES = [
 def test_mid_shapes(shape):
     cfg = synth.custom_config("mid", 200 + shape["T"], **shape)
     act, w_np, w_dev = _small_case(cfg)
-    print(f"[mid] {shape}", flush=True)
-    layer = _layer_for(cfg, w_dev, cfg.T)
-    res = run_steps(layer, *_device_inputs(act))
     ref = _oracle_for(cfg, act, w_np)
-    _check_full(cfg, act, res, ref, f"mid {shape}", w_np)
+    layouts = [False] + ([True] if cfg.I % 256 == 0 and cfg.H % 512 == 0 else [])
+    for tiled in layouts:
+        print(f"[mid] {shape} tiled={tiled}", flush=True)
+        layer = _layer_for(cfg, w_dev, cfg.T, tiled=tiled)
+        res = run_steps(layer, *_device_inputs(act))
+        _check_full(cfg, act, res, ref, f"mid {shape} tiled={tiled}", w_np)
+
+
+def _tiled_reference(w, ws, I, fc1):
+    """The tiled layout as the header describes it, built on the host."""
+    E, N, half_k = w.shape
+    K = 2 * half_k
+    n_cg, n_st = N // 512, K // 128
+    data = np.empty((E, n_cg, n_st, 2048, 16), np.uint8)
+    sc = np.empty((E, n_cg, n_st, 512, 4), np.uint8)
+    q = np.arange(2048)
+    chunk, l = q // 64, q % 64
+    r = 16 * chunk + l // 4
+    c = (l & 3) ^ ((l >> 3) & 3)
+    rr = np.arange(512)
+    for cg in range(n_cg):
+        def glob(rows):
+            if not fc1:
+                return 512 * cg + rows
+            u = 8 * cg + rows // 64
+            b = (rows // 16) % 4
+            return np.where(b < 2, 0, I) + 32 * u + 16 * (b % 2) + rows % 16
+        g_r, g_rr = glob(r), glob(rr)
+        for st in range(n_st):
+            v = w[:, g_r, :].reshape(E, 2048, half_k)
+            idx = st * 64 + 16 * c
+            data[:, cg, st] = np.stack([v[:, j, idx[j]:idx[j] + 16] for j in range(2048)], 1)
+            sc[:, cg, st] = ws[:, g_rr, 4 * st:4 * st + 4]
+    return data.reshape(w.shape), sc.reshape(ws.shape)
+
+
+@pytest.mark.parametrize("which", ["w13", "w2"])
+def test_prepack_matches_documented_layout(which):
+    m = _lib()
+    cfg = synth.custom_config("pp", 400, T=1, H=1024, I=512, E=3, K=1)
+    w = synth.make_expert_weights(cfg, device="cpu")
+    a, s = w[which], w[which + "_s"]
+    fn = m.moe_prepack_w13 if which == "w13" else m.moe_prepack_w2
+    ta, ts = fn(a.to(DEV), s.to(DEV))
+    torch.cuda.synchronize()
+    ra, rs = _tiled_reference(a.numpy(), s.numpy(), cfg.I, which == "w13")
+    assert np.array_equal(to_np(ta), ra)
+    assert np.array_equal(to_np(ts), rs)
 
 
 def test_masked_slots_empty_experts_and_idle_tokens():
@@ -262,15 +306,16 @@ def _sample_tokens(ids, cfg, n):
     return sorted(set(picks))[:n] if n < 3 else sorted(set(picks))
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
-def test_full_size_sampled(cid):
+@pytest.mark.parametrize("cid,tiled", [(1, True), (2, True), (3, True), (4, True), (1, False),
+                                       (3, False)])
+def test_full_size_sampled(cid, tiled):
     cfg = synth.CONFIGS[cid]
-    print(f"[full c{cid}] {cfg}", flush=True)
+    print(f"[full c{cid} tiled={tiled}] {cfg}", flush=True)
     w_all = full_size_weights()
     sl = slice(cfg.expert_offset, cfg.expert_offset + cfg.E_local)
     w_dev = {k: v[sl] for k, v in w_all.items()}
     act = synth.make_activations(cfg)
-    layer = _layer_for(cfg, w_dev, cfg.T)
+    layer = _layer_for(cfg, w_dev, cfg.T, tiled=tiled)
     res = run_steps(layer, *_device_inputs(act))
     # routing, quantisation and grouping: every element
     rid, rw = oracle.route(act["logits"], act["bias"], cfg.K, cfg.routed_scaling)
