@@ -28,24 +28,47 @@ WORKLOADS = {"tiny": 0, "decode_T8": 1, "batched_decode_T256": 2, "prefill_T8192
              "ep_share_T4096": 4}
 
 
-def _sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+# Sources of the FC kernels: a traffic figure is valid only for these bytes.
+FC_SOURCES = ("common.h", "fc_common.h", "tiled.h", "fc.hip", "fc_prefill.hip")
 
 
-def _traffic(kernel_src, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+def fc_source_sha():
+    h = hashlib.sha256()
+    for name in FC_SOURCES:
+        h.update(open(os.path.join(ROOT, "mxfp8_mxfp4_experts_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def _traffic(workload):
+    """HBM bytes per FC1 launch from committed rocprofv3 counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel's reading), if they
+    were taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "fc1_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
         rec = d.get(workload)
-        if rec and rec.get("source_sha256") == _sha(kernel_src):
+        if rec and rec.get("source_sha256") == fc_source_sha():
             return rec["hbm_bytes_per_launch"]
-    except Exception:
+    except (OSError, ValueError, KeyError):
         return None
     return None
+
+
+def copy_calibration():
+    """A plain device copy of known size (1 GiB read + 1 GiB written), three
+    times: the reference reading for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(cfg, act, weights_dev, topk_idx, topk_w, n_tokens=1):
@@ -73,10 +96,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_T8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -98,7 +126,8 @@ def main():
     logits = torch.from_numpy(act["logits"]).to(dev)
     bias = torch.from_numpy(act["bias"]).to(dev)
     layer = m.MoELayer(w["w13"], w["w13_s"], w["w2"], w["w2_s"], top_k=cfg.K, E=cfg.E,
-                       expert_offset=cfg.expert_offset, max_tokens=cfg.T)
+                       expert_offset=cfg.expert_offset, routed_scaling=cfg.routed_scaling,
+                       situ_alpha=cfg.situ_alpha, situ_beta=cfg.situ_beta, max_tokens=cfg.T)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f}s workload={args.workload}",
@@ -120,11 +149,11 @@ def main():
         if ev is not None:
             ev[0].record()
         B.moe_fc1_situ(xq, xs, K, layer.expert_offsets, sroute, layer.w13, layer.w13_s,
-                       layer.workspace, cfg.situ_alpha, cfg.situ_beta, hq, hs)
+                       layer.workspace, cfg.situ_alpha, cfg.situ_beta, hq, hs, tiled=layer.tiled)
         if ev is not None:
             ev[1].record()
         B.moe_fc2_combine(hq, hs, T, K, layer.expert_offsets, rrow, tw, layer.w2, layer.w2_s,
-                          layer.workspace, out)
+                          layer.workspace, out, tiled=layer.tiled)
 
     for _ in range(args.warmup):
         step()
@@ -144,6 +173,12 @@ def main():
     ms_per_step = start.elapsed_time(stop) / args.steps
     fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
+    # The timed calls must compute what the layer computes.
+    ref = layer(x, logits, bias)
+    if not torch.equal(ref.view(torch.int16), out.view(torch.int16)):
+        print("[bench] timed path disagrees with MoELayer", file=sys.stderr, flush=True)
+        sys.exit(1)
+
     # Algorithmic work of this batch.
     offs = layer.expert_offsets.cpu().numpy()
     n_kept = int(offs[-1])
@@ -156,10 +191,14 @@ def main():
     layer_bytes = (D * H * I * 1.59375 + 2 * T * H + 4 * T * cfg.E + 2 * 1.03125 * T * H
                    + 2 * 1.03125 * n_kept * I + 2 * T * H)
     layer_flops = n_kept * 6.0 * H * I
-    prefill = args.workload in ("prefill_T8192",)
-    src = os.path.join(ROOT, "mxfp8_mxfp4_experts_amd", "csrc", "fc.hip")
-    traffic = _traffic(src, args.workload)
-    if prefill:
+    traffic = _traffic(args.workload)
+    # The binding roof is the one with the longer ideal time at MI355X's
+    # published peaks (bytes / 8 TB/s against flops / 5 PFLOP/s).
+    t_hbm = fc1_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = fc1_flops / (MFMA_FP8_PEAK_TFLOPS * 1e12)
+    mfma_frac = fc1_flops / (fc1_ms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS
+    hbm_frac = fc1_bytes / (fc1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    if t_mfma > t_hbm:
         ach = fc1_flops / (fc1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_FP8_PEAK_TFLOPS, 4),
@@ -169,7 +208,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
     roof.update({"kernel": "fc1_situ", "kernel_ms": round(fc1_ms, 5),
-                 "algorithmic_bytes": int(fc1_bytes), "algorithmic_flops": fc1_flops})
+                 "algorithmic_bytes": int(fc1_bytes), "algorithmic_flops": fc1_flops,
+                 "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4)})
 
     res = {
         "metric": "MoE-layer tokens/s",

@@ -15,7 +15,7 @@ constexpr int kGroup = 32;          // MX block: one E8M0 scale per 32 elements
 
 // FC tile heights (token rows per workgroup tile) for which moe_permute
 // writes a tile prefix: 16 << i for i in [0, kNumTileSizes).
-constexpr int kNumTileSizes = 4;
+constexpr int kNumTileSizes = 5;
 
 // ---------------------------------------------------------------------------
 // Workspace layout shared by moe_permute / moe_fc1_situ / moe_fc2_combine.

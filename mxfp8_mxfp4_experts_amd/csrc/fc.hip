@@ -264,12 +264,8 @@ template <bool FC1>
 hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_cu, bool tiled,
                      hipStream_t stream) {
   const int avg = expected_rows(R, prm.E_local);
-  if (avg >= 32 && prefill_shape_ok(prm, FC1)) {
-    // Tile height 128 (prefix index 3); one 512-thread workgroup per CU.
-    prm.tile_prefix = tile_prefix_all + (size_t)3 * (prm.E_local + 1);
-    const int n_wg = (n_cu > 8 ? n_cu : 8) & ~7;
-    return launch_fc_prefill(FC1, tiled, prm, n_wg, stream);
-  }
+  if (avg >= 32 && prefill_shape_ok(prm, FC1))
+    return launch_fc_prefill(FC1, tiled, prm, tile_prefix_all, n_cu, stream);
   const int nt = avg <= 24 ? 1 : 2;
   prm.tile_prefix = tile_prefix_all + (size_t)(nt == 1 ? 0 : 1) * (prm.E_local + 1);
   const int tm = 16 * nt;

@@ -37,9 +37,22 @@ struct FcParams {
   float* y;                  // FC2 out [R, N]
 };
 
+// SiTU(g, u) = alpha tanh(g / alpha) sigmoid(g) * beta tanh(u / beta)
+// (page 1, "真实 checkpoint 契约": the SiTU activation with alpha = 4, beta =
+// 25), from the hardware base-2 exponential and reciprocal:
+//   sigmoid(g) = 1 / (1 + 2^(-g log2 e)),  tanh(y) = 1 - 2 / (1 + 2^(2 y log2 e)).
+// Each factor is within a few float32 ulps of its value (the tanh form loses
+// only absolute accuracy, ~1e-7, for small |y|), far below the E4M3 rounding
+// the result goes through next.  Infinite exponentials give the limits
+// (tanh -> +-1, sigmoid -> 0 or 1); NaN propagates.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_tanh(float y) {
+  return 1.0f - 2.0f * fast_rcp(1.0f + fast_exp2(y * 2.8853900817779268f));   // 2 log2 e
+}
 __device__ __forceinline__ float situ(float g, float u, float alpha, float beta) {
-  const float sig = 1.0f / (1.0f + __expf(-g));
-  return alpha * tanhf(g / alpha) * sig * (beta * tanhf(u / beta));
+  const float sig = fast_rcp(1.0f + fast_exp2(g * -1.4426950408889634f));     // -log2 e
+  return alpha * fast_tanh(g * fast_rcp(alpha)) * sig * (beta * fast_tanh(u * fast_rcp(beta)));
 }
 
 // Largest expert e with prefix[e] <= tile (the expert owning that tile).
@@ -59,6 +72,15 @@ __device__ __forceinline__ void pin_acc(v4f (&acc)[4]) {
   for (int bk = 0; bk < 4; ++bk)
 #pragma unroll
     for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(acc[bk][r]));
+}
+
+// The same for accumulators that live in AGPRs (kernels whose accumulators
+// fill the architectural VGPRs' counterpart file).
+__device__ __forceinline__ void pin_acc_agpr(v4f (&acc)[4]) {
+#pragma unroll
+  for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" : "+a"(acc[bk][r]));
 }
 
 // Epilogue of one wavefront unit (64 weight rows) for one 16-token sub-tile.

@@ -1,246 +1,341 @@
-// Prefill-shaped FC1 / FC2: LDS-staged tiles for MFMA operand reuse.
+// Prefill-shaped FC1 / FC2 (many grouped rows per expert).
 //
 // Same method as the decode-shaped kernel (page 1, "Serving 调用链": grouped
 // GEMM1 -> gated activation -> GEMM2; "真实 checkpoint 契约": [gate; up] halves,
-// SiTU(4, 25); page 5: w13 / w2 and scale layouts), tiled for many rows per
-// expert:
-//   * a workgroup (8 wavefronts) computes up to 128 grouped rows of one expert
-//     against 512 weight rows; wavefront (th, rg) owns token rows
-//     [64 th, 64 th + 64) and weight rows [128 rg, 128 rg + 128) = two units
-//     (FC1 unit: gate rows [c, c+32) with up rows [I+c, I+c+32));
-//   * K advances in 128-wide stages.  Three LDS buffers hold the weight slice
-//     (512 rows x 64 bytes), the token slice (128 rows x 128 bytes) and both
-//     operands' scale bytes.  They are filled by direct global -> LDS loads
-//     (global_load_lds_dwordx4), two stages ahead of the MFMAs, with no
-//     staging registers; every wavefront issues exactly 8 such loads per
-//     stage, so "s_waitcnt vmcnt(8)" leaves only the next stage in flight;
-//   * 16-byte LDS chunks are XOR-swizzled (weights by row bits 1..2, tokens by
-//     row bits 0..2) so the eight lanes served together hit eight bank
-//     groups; a lane's load source is permuted to match, since each load
-//     writes 1 KB of LDS in lane order;
-//   * tiles are variable height: the last tile of an expert holds the rest of
-//     its rows and wavefronts skip empty 16-row sub-tiles;
-//   * persistent grid: each XCD walks a contiguous range of work items
-//     (band of `band` column groups, tile, column group), so the tiles of one
-//     expert and the column groups of one tile run close together in that
-//     XCD's L2.
+// SiTU(4, 25); page 5: w13 / w2 and scale layouts), organised for experts
+// that hold tens to hundreds of grouped rows:
+//   * a workgroup of 4 wavefronts (one per SIMD, each with the whole register
+//     file) computes up to 256 grouped rows of one expert against 256 weight
+//     rows.  Wavefront w owns one 64-row unit (FC1: gate rows [c, c+32) with
+//     up rows [I+c, I+c+32), so SiTU pairs stay in one wavefront; FC2: 64
+//     output columns) and all 256 token rows: 4 row blocks x 16 token tiles
+//     of 16x16 accumulators, 256 AGPRs;
+//   * an expert with at most 256 rows is one tile, so its weights are read
+//     once in total; its token rows are re-read by every column group, which
+//     the XCD-contiguous schedule keeps in that XCD's L2.  The tiles of a hot
+//     expert run side by side on one column group, sharing its weights;
+//   * weights go from memory straight to registers: one coalesced 16-byte
+//     load per lane per 16-row block and stage (in the tiled layout each
+//     block's MFMA operand is one contiguous 1 KB piece in lane order), three
+//     stages ahead in rotating register sets;
+//   * token rows go through a ring of 4 LDS stages (256 rows x 128 bytes +
+//     one scale dword per row), filled by direct buffer -> LDS loads three
+//     stages ahead; 16-byte chunks are XOR-swizzled by row bits 0..2 so the
+//     eight lanes served together hit eight bank groups.  Every wavefront
+//     issues the same loads per stage (9 direct-to-LDS, 8 to registers), so
+//     one fixed "s_waitcnt vmcnt" leaves exactly the later stages in flight;
+//     past the last stage the final stage is reloaded to keep that count;
+//   * token tiles are taken in pairs; pairs past the expert's last row are
+//     skipped (at most one empty 16-row tile is computed);
+//   * buffer resources keep every per-lane address a 32-bit offset.
 #include "common.h"
 #include "fc_common.h"
 #include "launch.h"
 #include "tiled.h"
 
+#include <type_traits>
+
 namespace mi355moe {
 
 namespace {
 
-constexpr int kBM = 128;                    // token rows per tile
-constexpr int kBN = 512;                    // weight rows per tile (8 units)
+constexpr int kBM = 256;                    // token rows per tile
+constexpr int kBN = 256;                    // weight rows per tile (4 units)
 constexpr int kKS = 128;                    // K per stage
-constexpr int kWBytes = kBN * kKS / 2;      // 32768: E2M1 weight slice
-constexpr int kABytes = kBM * kKS;          // 16384: E4M3 token slice
-constexpr int kWSBytes = kBN * 4;           // 2048: one scale dword per weight row
-constexpr int kASBytes = kBM * 4;           // 512: one scale dword per token row
-constexpr int kOffA = kWBytes;
-constexpr int kOffWS = kOffA + kABytes;
-constexpr int kOffAS = kOffWS + kWSBytes;
-constexpr int kStage = kOffAS + kASBytes;   // 51712
-constexpr int kNumBuf = 3;
-constexpr int kThreads = 512;
+constexpr int kABytes = kBM * kKS;          // 32768: E4M3 token slice
+constexpr int kASBytes = kBM * 4;           // 1024: one scale dword per token row
+constexpr int kStage = kABytes + kASBytes;  // 33792
+constexpr int kNumBuf = 4;                  // LDS ring depth
+constexpr int kThreads = 256;
+constexpr int kTilePrefixIndex = 4;         // tile height 16 << 4 = 256
+constexpr int kNt = 2;                      // nontemporal policy for weight loads
+static_assert(kKS == kTileK && 2 * kBN == kTileRows, "tile shape");
+static_assert((16 << kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSizes, "tile prefix");
 
-static_assert(kBN == kTileRows && kKS == kTileK && kWBytes == kTileBytes, "tile shape");
+// Loads issued per wavefront and stage; the wait for stage s leaves the
+// weights of stage s and both later stages in flight.
+constexpr int kActLoads = 9, kWLoads = 8;
+constexpr int kWaitCount = 3 * kWLoads + 2 * kActLoads;   // 42
+static_assert(kWaitCount < 64, "vmcnt range");
 
-// Global row of the expert's weight matrix held at LDS row r (0..511) of
-// column group cg (the same assignment as the tiled layout).
-template <bool FC1>
-__device__ __forceinline__ int weight_row(int r, int cg, int I) {
-  return tiled_row<FC1>(r, cg, I);
+// Raw buffer resource: base and byte size in SGPRs.  Sizes stay below 2^31,
+// so kOutOfRange (plus any stage offset) is always past the end.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
 }
 
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-__device__ __forceinline__ void dma4(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [I, N).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
-// TILED: p.w / p.w_s hold the tiled layout (tiled.h), else the checkpoint
-// layout.
+// Weight operands of one stage for one wavefront: 4 row blocks.
+struct WStage {
+  v4i w[4];
+  int s[4];
+};
+
+// Token operands of one 16-row tile: K [16g, +16) and [64 + 16g, +16) for
+// lane group g, and the row's scale byte for MX block g.
+struct AOp {
+  v4i lo, hi;
+  int sc;
+};
+
 template <bool FC1, bool TILED>
-__global__ __launch_bounds__(kThreads) void fc_prefill_kernel(FcParams p, int n_cg, int band) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fc_prefill_kernel(FcParams p, int n_cg) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kNumBuf * kStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
-  const int th = wave >> 2, rg = wave & 3, g = lane >> 4, li = lane & 15;
+  const int g = lane >> 4, li = lane & 15;
   const int K = p.K;
   const int n_stages = K / kKS;
   const int* prefix = p.tile_prefix;
-  const int n_tiles = prefix[p.E_local];
-  const int n_bands = (n_cg + band - 1) / band;
-  const int per_band = n_tiles * band;
-  const int n_items = n_bands * per_band;
+  const int n_items = prefix[p.E_local] * n_cg;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
   const int item_lo = (int)((int64_t)n_items * xcd / 8);
   const int item_hi = (int)((int64_t)n_items * (xcd + 1) / 8);
+  const __amdgpu_buffer_rsrc_t act_r = rsrc(p.act, (uint32_t)(p.act_rows * K));
+  const __amdgpu_buffer_rsrc_t acts_r = rsrc(p.act_s, (uint32_t)(p.act_rows * (K / 32)));
 
+  // Items run expert by expert; inside an expert column group by column
+  // group, and inside a column group tile by tile: neighbouring items share
+  // either the weights (tiles of one hot expert) or the token rows (column
+  // groups of one tile).  Expert e owns items [n_cg prefix[e], n_cg prefix[e+1]).
   for (int item = item_lo + slot; item < item_hi; item += per_xcd) {
-    const int bnd = item / per_band, rem = item - bnd * per_band;
-    const int tile = rem / band, cg = bnd * band + rem % band;
-    if (cg >= n_cg) continue;
-    const int e = find_expert(prefix, p.E_local, tile);
-    const int row_begin = p.expert_offsets[e] + (tile - prefix[e]) * kBM;
+    const int e = __builtin_amdgcn_readfirstlane(find_expert(prefix, p.E_local, item / n_cg));
+    const int nt = prefix[e + 1] - prefix[e];
+    const int local = item - prefix[e] * n_cg;
+    const int cg = local / nt, t_in_e = local - cg * nt;
+    const int row_begin = p.expert_offsets[e] + t_in_e * kBM;
     const int n_valid = min(p.expert_offsets[e + 1] - row_begin, kBM);
+    const int npairs = (n_valid + 31) >> 5;                     // token tile pairs in use
+    const int unit = 4 * cg + wave;                             // global 64-row unit
 
-    // DMA sources of this lane.  Weights: wave w fills rows 64w + 16i + l/4,
-    // physical chunk l%4 <- logical chunk (l%4) ^ ((row >> 1) & 3) (in the
-    // tiled layout that is simply the next 16 bytes).  Tokens: rows
-    // 16w + 8i + l/8, physical chunk l%8 <- logical (l%8) ^ (row & 7).
-    // Scales: weight rows 64w + l; token rows 64w + l for waves 0 and 1.
-    const uint8_t* wsrc[4];
-    const uint8_t* asrc[2];
-    size_t wstep, wsstep;
-    const uint8_t* wssrc;
+    // Weights of row block i of this wavefront's unit (rows 16 i + li):
+    // lane offset + SGPR offset per block and stage.  Each lane reads only
+    // its scale byte (MX block 4 s + g of its row).
+    __amdgpu_buffer_rsrc_t w_r, ws_r;
+    uint32_t w_voff, ws_voff;
+    int w_soff[4], ws_soff[4], w_step, ws_step;
     if (TILED) {
-      const size_t blk0 = tiled_block(e, cg, 0, n_cg, n_stages);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wsrc[i] = p.w + blk0 * kTileBytes + (4 * wave + i) * 1024 + 16 * lane;
-      wssrc = p.w_s + blk0 * kTileScaleBytes + (64 * wave + lane) * 4;
-      wstep = kTileBytes;
-      wsstep = kTileScaleBytes;
-    } else {
-      const int wc = (lane & 3) ^ ((lane >> 3) & 3);
+      // 512-row group cg / 2 holds units 8 (cg / 2) .. + 7; this unit is its
+      // (4 (cg & 1) + wave)-th.
+      const int u8 = 4 * (cg & 1) + wave;
+      const size_t blk0 = tiled_block(e, cg >> 1, 0, n_cg >> 1, n_stages);
+      w_r = rsrc(p.w + blk0 * kTileBytes, (uint32_t)n_stages * kTileBytes);
+      ws_r = rsrc(p.w_s + blk0 * kTileScaleBytes, (uint32_t)n_stages * kTileScaleBytes);
+      w_voff = 4096 * u8 + 16 * (4 * li + (g ^ ((li >> 1) & 3)));
+      ws_voff = 4 * (64 * u8 + li) + g;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wave + 16 * i + (lane >> 2);
-        wsrc[i] = p.w + ((size_t)e * p.N + weight_row<FC1>(r, cg, p.I)) * (K / 2) + 16 * wc;
+        w_soff[i] = 1024 * i;
+        ws_soff[i] = 64 * i;
       }
-      wssrc = p.w_s + ((size_t)e * p.N + weight_row<FC1>(64 * wave + lane, cg, p.I)) * (K / 32);
-      wstep = 64;
-      wsstep = 4;
-    }
-    const int ac = (lane & 7) ^ ((lane >> 3) & 7);
+      w_step = kTileBytes;
+      ws_step = kTileScaleBytes;
+    } else {
+      const size_t e_rows = (size_t)e * p.N;
+      w_r = rsrc(p.w + e_rows * (K / 2), (uint32_t)p.N * (K / 2));
+      ws_r = rsrc(p.w_s + e_rows * (K / 32), (uint32_t)p.N * (K / 32));
+      w_voff = li * (K / 2) + 16 * g;
+      ws_voff = li * (K / 32) + g;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = 16 * wave + 8 * i + (lane >> 3);
-      const int row = row_begin + min(tok, n_valid - 1);
-      const size_t src = FC1 ? (size_t)(p.gather[row] / p.top_k) : (size_t)row;
-      asrc[i] = p.act + src * K + 16 * ac;
+      for (int i = 0; i < 4; ++i) {
+        // FC1: blocks 0, 1 are gate rows 32 unit + 16 i, blocks 2, 3 the
+        // matching up rows I + 32 unit + 16 (i - 2); FC2: rows 64 unit + 16 i.
+        const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * unit + 16 * (i & 1) : 64 * unit + 16 * i;
+        w_soff[i] = rb * (K / 2);
+        ws_soff[i] = rb * (K / 32);
+      }
+      w_step = 64;
+      ws_step = 4;
     }
-    const uint8_t* assrc;
+    // Token rows: wavefront w fills rows 64 w + 8 i + l / 8 (i < 8); physical
+    // chunk l % 8 of a row takes logical chunk (l % 8) ^ (row & 7).  Scale
+    // dwords: rows 64 w + l.  Rows past the expert's last, inside the last
+    // tile pair, repeat that row; rows of skipped pairs get an offset past
+    // the buffer's end, which the buffer unit answers with zeros without
+    // touching memory (so every wavefront still issues the same loads).
+    uint32_t a_voff[8];
+    const int ac = (lane & 7) ^ ((lane >> 3) & 7);
+    const int rows_used = 32 * npairs;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tok = 64 * wave + 8 * i + (lane >> 3);
+      const int row = row_begin + min(tok, n_valid - 1);
+      const int src = FC1 ? p.gather[row] / p.top_k : row;
+      a_voff[i] = tok < rows_used ? (uint32_t)src * K + 16 * ac : kOutOfRange;
+    }
+    uint32_t as_voff;
     {
-      const int tok = 64 * (wave & 1) + lane;
+      const int tok = 64 * wave + lane;
       const int row = row_begin + min(tok, n_valid - 1);
-      const size_t src = FC1 ? (size_t)(p.gather[row] / p.top_k) : (size_t)row;
-      assrc = p.act_s + src * (K / 32);
+      const int src = FC1 ? p.gather[row] / p.top_k : row;
+      as_voff = tok < rows_used ? (uint32_t)src * (K / 32) : kOutOfRange;
     }
-    const bool loads_act_scales = wave < 2;
-    auto issue = [&](int s) {
+
+    auto issue_act = [&](int s) __attribute__((always_inline)) {
+      const int sc = min(s, n_stages - 1);
       uint8_t* base = lds + (s % kNumBuf) * kStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(wsrc[i] + (size_t)s * wstep, base + wave * 4096 + i * 1024);
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + wave * 8192 + i * 1024, 16,
+                                                 a_voff[i], kKS * sc, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(acts_r, base + kABytes + wave * 256, 4, as_voff,
+                                               4 * sc, 0, 0);
+    };
+    auto load_w = [&](WStage& ws, int s) __attribute__((always_inline)) {
+      const int sc = min(s, n_stages - 1);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(asrc[i] + (size_t)s * 128, base + kOffA + wave * 2048 + i * 1024);
-      dma4(wssrc + (size_t)s * wsstep, base + kOffWS + wave * 256);
-      if (loads_act_scales) dma4(assrc + (size_t)s * 4, base + kOffAS + wave * 256);
+      for (int i = 0; i < 4; ++i)
+        ws.w[i] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(w_r, w_voff, w_soff[i] + sc * w_step, kNt));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ws.s[i] = __builtin_amdgcn_raw_buffer_load_b8(ws_r, ws_voff, ws_soff[i] + sc * ws_step, 0);
     };
 
-    const int nsub = max(0, min(4, (n_valid - th * 64 + 15) >> 4));
-    v4f acc[4][2][4];
+    v4f acc[16][4];  // [token tile][row block]
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < 16; ++tt)
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-        for (int bk = 0; bk < 4; ++bk) acc[tt][uu][bk] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) acc[tt][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    issue(0);
-    if (n_stages > 1) issue(1);
-    for (int s = 0; s < n_stages; ++s) {
-      // This wavefront's loads of stage s are done once at most the next
-      // stage's remain (8 loads per stage for waves 0 and 1, 7 for the
-      // others); the barrier extends that to every wavefront and also means
-      // everyone has finished stage s - 1, whose buffer the loads of stage
-      // s + 2 now overwrite.
-      if (s + 1 < n_stages) {
-        if (loads_act_scales) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+    // Token operands of tile tt from LDS stage buffer A.
+    auto read_a = [&](AOp& o, const uint8_t* A, int tt) __attribute__((always_inline)) {
+      const int tok = tt * 16 + li;
+      const uint8_t* arow = A + tok * kKS;
+      o.lo = *reinterpret_cast<const v4i*>(arow + 16 * (g ^ (li & 7)));
+      o.hi = *reinterpret_cast<const v4i*>(arow + 16 * ((4 + g) ^ (li & 7)));
+      o.sc = A[kABytes + 4 * tok + g];
+    };
+
+    auto compute = [&](const WStage& ws, int s) __attribute__((always_inline)) {
+      // The stage offset is made opaque so that the compiler cannot prove the
+      // reads of later tile pairs in bounds and hoist them all above the pair
+      // conditions (which would hold every pair's operands at once).
+      int stage_off = (s % kNumBuf) * kStage;
+      asm volatile("" : "+s"(stage_off));
+      const uint8_t* A = lds + stage_off;
+      AOp buf[2][2];   // [pair parity][tile of the pair]
+      read_a(buf[0][0], A, 0);
+      read_a(buf[0][1], A, 1);
+      auto pair_fn = [&](auto ppi) __attribute__((always_inline)) {
+        constexpr int pp = decltype(ppi)::value;
+        if (pp < npairs) {
+          if constexpr (pp + 1 < 8) {
+            read_a(buf[(pp + 1) & 1][0], A, 2 * pp + 2);
+            read_a(buf[(pp + 1) & 1][1], A, 2 * pp + 3);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const AOp& o = buf[pp & 1][h];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[2 * pp + h][i] = mfma_w4a8<0>(ws.w[i], o.lo, o.hi, acc[2 * pp + h][i], ws.s[i], o.sc);
+          }
+          // Keep this pair's MFMAs inside its condition, in this order (the
+          // compiler would otherwise sink them below the later pairs' reads).
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[2 * pp + h][i]));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      static_for<0, 8>(pair_fn);
+    };
+
+    auto step = [&](WStage& cur, int s) __attribute__((always_inline)) {
+      // Token rows of stage s have landed for this wavefront; the barrier
+      // extends that to all wavefronts and tells that stage s - 1 is done
+      // everywhere, so its buffer can take stage s + 3.
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");
       asm volatile("s_barrier" ::: "memory");
-      if (s + 2 < n_stages) issue(s + 2);
-      const uint8_t* W = lds + (s % kNumBuf) * kStage;
-      const uint8_t* A = W + kOffA;
-      const int* WS = reinterpret_cast<const int*>(W + kOffWS);
-      const int* AS = reinterpret_cast<const int*>(W + kOffAS);
-      // Slice K [128 s, +128): slot b is MX block 4 s + b.
-      v4i wv[2][4];
-      int wsc[2][4];
-#pragma unroll
-      for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-        for (int bk = 0; bk < 4; ++bk) {
-          const int r = 128 * rg + 64 * uu + 16 * bk + li;
-          wv[uu][bk] = *reinterpret_cast<const v4i*>(W + r * 64 + 16 * (g ^ ((li >> 1) & 3)));
-          wsc[uu][bk] = WS[r] >> (8 * g);
-        }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (tt < nsub) {
-          const int tok = th * 64 + tt * 16 + li;
-          const uint8_t* arow = A + tok * 128;
-          const v4i lo = *reinterpret_cast<const v4i*>(arow + 16 * (g ^ (li & 7)));
-          const v4i hi = *reinterpret_cast<const v4i*>(arow + 16 * ((4 + g) ^ (li & 7)));
-          const int asc = AS[tok] >> (8 * g);
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu)
-#pragma unroll
-            for (int bk = 0; bk < 4; ++bk)
-              acc[tt][uu][bk] = mfma_w4a8<0>(wv[uu][bk], lo, hi, acc[tt][uu][bk], wsc[uu][bk], asc);
-        }
-      }
+      issue_act(s + 3);
+      asm volatile("" ::: "memory");
+      compute(cur, s);
+      asm volatile("" ::: "memory");
+      load_w(cur, s + 3);
+      asm volatile("" ::: "memory");
+    };
+    WStage w0, w1, w2;
+    issue_act(0);
+    asm volatile("" ::: "memory");
+    load_w(w0, 0);
+    asm volatile("" ::: "memory");
+    issue_act(1);
+    asm volatile("" ::: "memory");
+    load_w(w1, 1);
+    asm volatile("" ::: "memory");
+    issue_act(2);
+    asm volatile("" ::: "memory");
+    load_w(w2, 2);
+    asm volatile("" ::: "memory");
+    // Stage loop, unrolled by 3 so each register set keeps a fixed name.
+    int s = 0;
+    for (; s + 3 <= n_stages; s += 3) {
+      step(w0, s);
+      step(w1, s + 1);
+      step(w2, s + 2);
     }
-    // Everyone is done with the LDS buffers before the next item refills them.
+    if (s < n_stages) step(w0, s);
+    if (s + 1 < n_stages) step(w1, s + 1);
+    // Drain the reloads issued past the end before the ring is reused.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
 
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      pin_acc(acc[tt][0]);
-      pin_acc(acc[tt][1]);
-    }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (tt < nsub) {
-        const int t_in = th * 64 + tt * 16 + li;
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu)
-          store_subtile<FC1>(p, acc[tt][uu], row_begin + t_in, t_in < n_valid,
-                             cg * 8 + 2 * rg + uu, g);
+    auto pin = [&](auto tti) __attribute__((always_inline)) {
+      pin_acc_agpr(acc[decltype(tti)::value]);
+    };
+    static_for<0, 16>(pin);
+    auto epi = [&](auto tti) __attribute__((always_inline)) {
+      constexpr int tt = decltype(tti)::value;
+      if (2 * npairs > tt) {
+        const int t_in = tt * 16 + li;
+        store_subtile<FC1>(p, acc[tt], row_begin + t_in, t_in < n_valid, unit, g);
       }
-    }
+    };
+    static_for<0, 16>(epi);
   }
 }
 
 }  // namespace
 
 bool prefill_shape_ok(const FcParams& prm, bool fc1) {
-  // FC1: 256 intermediate columns (512 w13 rows) per tile; FC2: 512 output
-  // columns.
-  return prm.K % kKS == 0 && (fc1 ? prm.I % 256 == 0 : prm.N % kBN == 0);
+  // FC1: 128 intermediate columns (256 w13 rows) per tile and whole 512-row
+  // groups of the tiled layout (I % 256); FC2: 256 output columns per tile,
+  // whole 512-row groups (H % 512).  Buffer offsets are 32-bit: the
+  // activation array and one expert's weights must each stay below 2 GiB.
+  const int64_t K = prm.K;
+  return K % kKS == 0 && (fc1 ? prm.I % 256 == 0 : prm.N % 512 == 0) &&
+         prm.act_rows * K < ((int64_t)1 << 31) && (int64_t)prm.N * (K / 2) < ((int64_t)1 << 31);
 }
 
-hipError_t launch_fc_prefill(bool fc1, bool tiled, const FcParams& prm, int n_wg,
-                             hipStream_t stream) {
-  const int n_cg = fc1 ? prm.I / 256 : prm.N / kBN;
-  const int band = 2;
+hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* tile_prefix_all,
+                             int n_cu, hipStream_t stream) {
+  prm.tile_prefix = tile_prefix_all + (size_t)kTilePrefixIndex * (prm.E_local + 1);
+  const int n_cg = fc1 ? prm.I / 128 : prm.N / kBN;
+  // Persistent grid: one workgroup per CU, a multiple of the 8 XCDs.
+  const int n_wg = (n_cu > 8 ? n_cu : 8) & ~7;
   const dim3 grid(n_wg), block(kThreads);
   if (fc1 && tiled)
-    hipLaunchKernelGGL((fc_prefill_kernel<true, true>), grid, block, 0, stream, prm, n_cg, band);
+    hipLaunchKernelGGL((fc_prefill_kernel<true, true>), grid, block, 0, stream, prm, n_cg);
   else if (fc1)
-    hipLaunchKernelGGL((fc_prefill_kernel<true, false>), grid, block, 0, stream, prm, n_cg, band);
+    hipLaunchKernelGGL((fc_prefill_kernel<true, false>), grid, block, 0, stream, prm, n_cg);
   else if (tiled)
-    hipLaunchKernelGGL((fc_prefill_kernel<false, true>), grid, block, 0, stream, prm, n_cg, band);
+    hipLaunchKernelGGL((fc_prefill_kernel<false, true>), grid, block, 0, stream, prm, n_cg);
   else
-    hipLaunchKernelGGL((fc_prefill_kernel<false, false>), grid, block, 0, stream, prm, n_cg, band);
+    hipLaunchKernelGGL((fc_prefill_kernel<false, false>), grid, block, 0, stream, prm, n_cg);
   return hipGetLastError();
 }
 

@@ -24,11 +24,11 @@ hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                       hipStream_t stream);
 struct FcParams;
 // Prefill-shaped FC kernels (fc_prefill.hip): usable when K % 128 == 0, the
-// output columns split into 512-row weight tiles and the operands fit 32-bit
-// buffer offsets.
+// weight rows split into whole 512-row groups and the operands fit 32-bit
+// buffer offsets.  They read the 256-row tile prefix.
 bool prefill_shape_ok(const FcParams& prm, bool fc1);
-hipError_t launch_fc_prefill(bool fc1, bool tiled, const FcParams& prm, int n_wg,
-                             hipStream_t stream);
+hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* tile_prefix_all,
+                             int n_cu, hipStream_t stream);
 // One-time reordering of checkpoint-layout weights into the tiled layout.
 hipError_t launch_prepack(bool fc1, const uint8_t* w, const uint8_t* ws, int E_local, int N,
                           int K, int I, uint8_t* tw, uint8_t* tws, hipStream_t stream);

@@ -7,7 +7,7 @@
 // One workgroup of 1024 threads:
 //  1. histogram of local expert ids in LDS;
 //  2. block-wide exclusive scans of the counts and of the per-expert tile
-//     counts for the FC tile heights 16, 32, 64 and 128 rows;
+//     counts for the FC tile heights 16, 32, 64, 128 and 256 rows;
 //  3. one wavefront walks the routes in ascending order, 64 at a time:
 //     lanes with the same expert find each other with ballots over the id
 //     bits, the lowest such lane reserves their rows from the expert's LDS
@@ -47,7 +47,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   // Each thread owns a contiguous run of experts.
   const int per = (E_local + kPermThreads - 1) / kPermThreads;
   const int e0 = tid * per;
-  int local[kScanVals] = {0, 0, 0, 0, 0};
+  int local[kScanVals];
+#pragma unroll
+  for (int v = 0; v < kScanVals; ++v) local[v] = 0;
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     int c = cnt[e];
     local[0] += c;
@@ -69,7 +71,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
   __syncthreads();
   if (tid == 0) {
-    int run[kScanVals] = {0, 0, 0, 0, 0};
+    int run[kScanVals];
+    for (int v = 0; v < kScanVals; ++v) run[v] = 0;
     for (int w = 0; w < kPermWaves; ++w)
       for (int v = 0; v < kScanVals; ++v) {
         int x = wave_tot[w][v];
