@@ -129,8 +129,9 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int top_k, int expert_o
   if (s != MOE_OK) return s;
   WsLayout l = ws_layout(T, top_k, E_local, 0);
   int32_t* prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.tile_prefix);
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.perm_counts);
   return finish(launch_permute(topk_idx, T * top_k, expert_offset, E_local, expert_offsets,
-                               sorted_route, route_row, prefix, stream));
+                               sorted_route, route_row, prefix, counts, stream));
 }
 
 static moe_status_t fc1_impl(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,

@@ -19,8 +19,14 @@ constexpr int kNumTileSizes = 5;
 
 // ---------------------------------------------------------------------------
 // Workspace layout shared by moe_permute / moe_fc1_situ / moe_fc2_combine.
+// Routes per chunk of the multi-workgroup grouping (moe_permute on large
+// batches): one wavefront ranks one chunk.
+constexpr int kPermChunk = 2048;
+inline int perm_chunks(int64_t R) { return (int)((R + kPermChunk - 1) / kPermChunk); }
+
 struct WsLayout {
   size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1]
+  size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
   size_t y;             // float [T * top_k][H]  (FC2 rows before the combine)
   size_t total;
 };
@@ -32,6 +38,8 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H) {
   size_t off = 0;
   l.tile_prefix = off;
   off = align256(off + sizeof(int32_t) * kNumTileSizes * (size_t)(E_local + 1));
+  l.perm_counts = off;
+  off = align256(off + sizeof(int32_t) * (size_t)perm_chunks((int64_t)T * top_k) * E_local);
   l.y = off;
   off = align256(off + sizeof(float) * (size_t)T * top_k * H);
   l.total = off;

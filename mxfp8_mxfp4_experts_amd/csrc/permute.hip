@@ -4,7 +4,12 @@
 // experts and maps global ids into it; "Phase 2 correctness harness": masked
 // -1 slots and empty experts are part of the contract.
 //
-// One workgroup of 1024 threads:
+// Result (both paths below give the same bytes): the kept routes of local
+// expert e occupy grouped rows [offs[e], offs[e+1]) in ascending route order;
+// sorted_route[row] = route, route_row[route] = row or -1; grouped rows past
+// the kept count hold -1; tile prefixes for the FC tile heights 16..256.
+//
+// Small batches: one workgroup of 1024 threads
 //  1. histogram of local expert ids in LDS;
 //  2. block-wide exclusive scans of the counts and of the per-expert tile
 //     counts for the FC tile heights 16, 32, 64, 128 and 256 rows;
@@ -13,6 +18,11 @@
 //     bits, the lowest such lane reserves their rows from the expert's LDS
 //     cursor, and each lane takes base + its rank among them.  This keeps
 //     the (token, slot) order inside every expert.
+// Large batches: the routes are cut into chunks of kPermChunk; a count
+// kernel writes each chunk's histogram, one workgroup turns the histograms
+// into expert offsets, tile prefixes and each chunk's first row per expert,
+// and a rank kernel (one wavefront per chunk) runs step 3 on its chunk from
+// those starting rows.
 #include "common.h"
 #include "launch.h"
 
@@ -142,14 +152,170 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
 }
 
+// Local expert of route r, or -1 (masked slot or outside the window).
+__device__ __forceinline__ int local_expert(const int32_t* idx, int r, int R, int offset,
+                                            int E_local) {
+  if (r >= R) return -1;
+  const int g = idx[r];
+  const int l = g - offset;
+  return (g >= 0 && l >= 0 && l < E_local) ? l : -1;
+}
+
+// Histogram of one chunk's local expert ids.
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx, int R,
+                                                         int offset, int E_local,
+                                                         int32_t* __restrict__ counts) {
+  extern __shared__ int cnt_s[];
+  const int c = blockIdx.x;
+  for (int e = threadIdx.x; e < E_local; e += 256) cnt_s[e] = 0;
+  __syncthreads();
+  const int r0 = c * kPermChunk;
+  for (int r = r0 + threadIdx.x; r < r0 + kPermChunk; r += 256) {
+    const int l = local_expert(idx, r, R, offset, E_local);
+    if (l >= 0) atomicAdd(&cnt_s[l], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E_local; e += 256) counts[(size_t)c * E_local + e] = cnt_s[e];
+}
+
+// Chunk histograms -> per-chunk starting rows (in place), expert offsets,
+// tile prefixes; grouped rows past the kept count get -1.
+__global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
+    int R, int E_local, int n_chunks, int32_t* __restrict__ counts,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_route,
+    int32_t* __restrict__ tile_prefix) {
+  __shared__ int wave_tot[kPermWaves][kScanVals];
+  __shared__ int n_kept_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Each thread owns a contiguous run of experts: their totals first.
+  const int per = (E_local + kPermThreads - 1) / kPermThreads;
+  const int e0 = tid * per;
+  int local[kScanVals];
+#pragma unroll
+  for (int v = 0; v < kScanVals; ++v) local[v] = 0;
+  for (int e = e0; e < e0 + per && e < E_local; ++e) {
+    int total = 0;
+    for (int c = 0; c < n_chunks; ++c) total += counts[(size_t)c * E_local + e];
+    local[0] += total;
+#pragma unroll
+    for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += (total + (16 << i) - 1) >> (4 + i);
+  }
+  int incl[kScanVals];
+#pragma unroll
+  for (int v = 0; v < kScanVals; ++v) {
+    int x = local[v];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    incl[v] = x;
+    if (lane == 63) wave_tot[wave][v] = x;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run[kScanVals];
+    for (int v = 0; v < kScanVals; ++v) run[v] = 0;
+    for (int w = 0; w < kPermWaves; ++w)
+      for (int v = 0; v < kScanVals; ++v) {
+        const int x = wave_tot[w][v];
+        wave_tot[w][v] = run[v];
+        run[v] += x;
+      }
+    n_kept_s = run[0];
+    expert_offsets[E_local] = run[0];
+    for (int i = 0; i < kNumTileSizes; ++i) tile_prefix[i * (E_local + 1) + E_local] = run[1 + i];
+  }
+  __syncthreads();
+  int excl[kScanVals];
+#pragma unroll
+  for (int v = 0; v < kScanVals; ++v) excl[v] = incl[v] - local[v] + wave_tot[wave][v];
+  // Then each expert's offset, its chunks' absolute starting rows and its
+  // tile prefixes.
+  for (int e = e0; e < e0 + per && e < E_local; ++e) {
+    expert_offsets[e] = excl[0];
+    int row = excl[0];
+    for (int c = 0; c < n_chunks; ++c) {
+      const int x = counts[(size_t)c * E_local + e];
+      counts[(size_t)c * E_local + e] = row;
+      row += x;
+    }
+    const int total = row - excl[0];
+    excl[0] = row;
+#pragma unroll
+    for (int i = 0; i < kNumTileSizes; ++i) {
+      tile_prefix[i * (E_local + 1) + e] = excl[1 + i];
+      excl[1 + i] += (total + (16 << i) - 1) >> (4 + i);
+    }
+  }
+  const int n_kept = n_kept_s;
+  for (int r = n_kept + tid; r < R; r += kPermThreads) sorted_route[r] = -1;
+}
+
+// Step 3 on one chunk, from the chunk's starting rows.
+__global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ idx, int R,
+                                                       int offset, int E_local,
+                                                       const int32_t* __restrict__ starts,
+                                                       int32_t* __restrict__ sorted_route,
+                                                       int32_t* __restrict__ route_row) {
+  extern __shared__ int cursor_s[];
+  const int c = blockIdx.x, lane = threadIdx.x;
+  for (int e = lane; e < E_local; e += 64) cursor_s[e] = starts[(size_t)c * E_local + e];
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E_local) ++nbits;
+  const int r0 = c * kPermChunk;
+  const int r_end = min(r0 + kPermChunk, R);
+  for (int base = r0; base < r_end; base += 64) {
+    const int r = base + lane;
+    const int l = local_expert(idx, r, r_end, offset, E_local);
+    const bool kept = l >= 0;
+    uint64_t peers = __ballot(kept);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = kept && ((l >> bit) & 1);
+      const uint64_t m = __ballot(set);
+      peers &= set ? m : ~m;
+    }
+    const uint64_t lower = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int rank = __popcll(peers & lower);
+    const int leader = kept ? (__ffsll((long long)peers) - 1) : lane;
+    int start = 0;
+    if (kept && leader == lane) {
+      start = cursor_s[l];
+      cursor_s[l] = start + __popcll(peers);
+    }
+    start = __shfl(start, leader);
+    if (r < r_end) {
+      if (kept) {
+        const int pos = start + rank;
+        sorted_route[pos] = r;
+        route_row[r] = pos;
+      } else {
+        route_row[r] = -1;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, int32_t* offs,
                           int32_t* sorted_route, int32_t* route_row, int32_t* tile_prefix,
-                          hipStream_t stream) {
-  size_t lds = sizeof(int) * 2 * (size_t)E_local;
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, stream, idx, R, offset,
-                     E_local, offs, sorted_route, route_row, tile_prefix);
+                          int32_t* counts, hipStream_t stream) {
+  if (R <= kPermChunk) {
+    const size_t lds = sizeof(int) * 2 * (size_t)E_local;
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, stream, idx, R, offset,
+                       E_local, offs, sorted_route, route_row, tile_prefix);
+    return hipGetLastError();
+  }
+  const int n_chunks = perm_chunks(R);
+  const size_t lds = sizeof(int) * (size_t)E_local;
+  hipLaunchKernelGGL(perm_count_kernel, dim3(n_chunks), dim3(256), lds, stream, idx, R, offset,
+                     E_local, counts);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, R, E_local,
+                     n_chunks, counts, offs, sorted_route, tile_prefix);
+  hipLaunchKernelGGL(perm_rank_kernel, dim3(n_chunks), dim3(64), lds, stream, idx, R, offset,
+                     E_local, counts, sorted_route, route_row);
   return hipGetLastError();
 }
 

@@ -105,10 +105,12 @@ MID_SHAPES = [
     # many experts, few rows each (decode-like tiles)
     dict(T=5, H=1024, I=512, E=64, K=8),
     dict(T=64, H=384, I=256, E=32, K=2, bias_kind="zero"),
-    # many rows per expert: the LDS-tiled prefill kernels (K % 256 == 0), with
-    # experts spanning several 128-row tiles plus a partial last tile
+    # many rows per expert: the prefill kernels (256-row tiles), with experts
+    # spanning several tiles plus a partial last tile
     dict(T=600, H=1024, I=512, E=8, K=2),
     dict(T=700, H=768, I=256, E=32, K=4, E_local=8, expert_offset=16),
+    # more than one grouping chunk (2048 routes) and ~600 rows per expert
+    dict(T=1200, H=512, I=256, E=6, K=3),
 ]
 
 
@@ -165,6 +167,32 @@ def test_prepack_matches_documented_layout(which):
     ra, rs = _tiled_reference(a.numpy(), s.numpy(), cfg.I, which == "w13")
     assert np.array_equal(to_np(ta), ra)
     assert np.array_equal(to_np(ts), rs)
+
+
+@pytest.mark.parametrize("T,K,E,E_local,offset", [
+    (200, 8, 600, 300, 100),      # one workgroup (at most 2048 routes)
+    (5000, 8, 600, 300, 100),     # chunked grouping: 20 chunks, ragged last one
+    (4096, 16, 64, 64, 0),        # exactly 32 chunks, every expert hot
+])
+def test_grouping_matches_oracle(T, K, E, E_local, offset):
+    """Grouping alone, bit-exact: masked slots, ids outside the local window
+    and empty experts, on both the single-workgroup and the chunked path."""
+    m = _lib()
+    rng = np.random.default_rng(7 + T)
+    # Skewed ids so some experts are empty and some span many chunks.
+    p = rng.dirichlet(np.full(E, 0.3))
+    idx = rng.choice(E, size=(T, K), p=p).astype(np.int32)
+    idx[rng.random((T, K)) < 0.05] = -1
+    print(f"[grouping] T={T} K={K} E={E} E_local={E_local} offset={offset}", flush=True)
+    ws = torch.empty(m.moe_workspace_size(T, K, E_local, 128, 128), dtype=torch.uint8, device=DEV)
+    offs, sroute, rrow = m.moe_permute(torch.from_numpy(idx).to(DEV), offset, E_local, ws)
+    torch.cuda.synchronize()
+    r_offs, r_sroute, r_rrow = oracle.permute(idx, offset, E_local)
+    n = int(r_offs[-1])
+    assert np.array_equal(to_np(offs), r_offs)
+    assert np.array_equal(to_np(sroute)[:n], r_sroute)
+    assert np.all(to_np(sroute)[n:] == -1)
+    assert np.array_equal(to_np(rrow), r_rrow)
 
 
 def test_masked_slots_empty_experts_and_idle_tokens():
