@@ -75,6 +75,9 @@ __device__ __forceinline__ void static_for(F& f) {
   }
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_t;
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+
 // Weight operands of one stage for one wavefront: 4 row blocks.
 struct WStage {
   v4i w[4];
@@ -92,6 +95,7 @@ template <bool FC1, bool TILED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fc_prefill_kernel(FcParams p, int n_cg) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kNumBuf * kStage];
+  lds_t* const lds_base = (lds_t*)lds;   // LDS address space: immediate offsets fold
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int g = lane >> 4, li = lane & 15;
@@ -209,63 +213,87 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[tt][i] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Token operands of tile tt from LDS stage buffer A.
-    auto read_a = [&](AOp& o, const uint8_t* A, int tt) __attribute__((always_inline)) {
-      const int tok = tt * 16 + li;
-      const uint8_t* arow = A + tok * kKS;
-      o.lo = *reinterpret_cast<const v4i*>(arow + 16 * (g ^ (li & 7)));
-      o.hi = *reinterpret_cast<const v4i*>(arow + 16 * ((4 + g) ^ (li & 7)));
-      o.sc = A[kABytes + 4 * tok + g];
+    // Token operands of tile tt from stage buffer A: lane parts of the
+    // addresses here, the tile's part (2048 tt, or 64 tt for the scale byte)
+    // goes into the LDS instructions' immediate offset.
+    const int a_lo = li * kKS + 16 * (g ^ (li & 7));
+    const int a_hi = li * kKS + 16 * ((4 + g) ^ (li & 7));
+    const int a_sc = kABytes + 4 * li + g;
+    auto read_a = [&](AOp& o, const lds_t* A, int tt) __attribute__((always_inline)) {
+      o.lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 2048 * tt);
+      o.hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 2048 * tt);
+      o.sc = A[a_sc + 64 * tt];
+    };
+    // Stage buffer of stage s.  The offset is made opaque so that the compiler
+    // cannot prove later pairs' reads in bounds and hoist them above the pair
+    // conditions (which would hold every pair's operands at once).
+    auto stage_buf = [&](int s) __attribute__((always_inline)) {
+      int off = (s % kNumBuf) * kStage;
+      asm volatile("" : "+s"(off));
+      return static_cast<const lds_t*>(lds_base) + off;
     };
 
-    auto compute = [&](const WStage& ws, int s) __attribute__((always_inline)) {
-      // The stage offset is made opaque so that the compiler cannot prove the
-      // reads of later tile pairs in bounds and hoist them all above the pair
-      // conditions (which would hold every pair's operands at once).
-      int stage_off = (s % kNumBuf) * kStage;
-      asm volatile("" : "+s"(stage_off));
-      const uint8_t* A = lds + stage_off;
-      AOp buf[2][2];   // [pair parity][tile of the pair]
-      read_a(buf[0][0], A, 0);
-      read_a(buf[0][1], A, 1);
+    AOp buf[2][2];   // [pair parity][tile of the pair]
+    // One stage: pair pp's 8 MFMAs, each followed by one LDS read of pair
+    // pp + 1 (6 reads), so the reads hide under the MFMAs.  Pair 0's operands
+    // were read before the call.
+    auto compute = [&](const WStage& ws, const lds_t* A) __attribute__((always_inline)) {
       auto pair_fn = [&](auto ppi) __attribute__((always_inline)) {
         constexpr int pp = decltype(ppi)::value;
         if (pp < npairs) {
-          if constexpr (pp + 1 < 8) {
-            read_a(buf[(pp + 1) & 1][0], A, 2 * pp + 2);
-            read_a(buf[(pp + 1) & 1][1], A, 2 * pp + 3);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          AOp(&cur)[2] = buf[pp & 1];
+          AOp(&nxt)[2] = buf[(pp + 1) & 1];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const AOp& o = buf[pp & 1][h];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[2 * pp + h][i] = mfma_w4a8<0>(ws.w[i], o.lo, o.hi, acc[2 * pp + h][i], ws.s[i], o.sc);
+          for (int j = 0; j < 8; ++j) {
+            const int h = j >> 2, i = j & 3;
+            acc[2 * pp + h][i] =
+                mfma_w4a8<0>(ws.w[i], cur[h].lo, cur[h].hi, acc[2 * pp + h][i], ws.s[i], cur[h].sc);
+            if constexpr (pp + 1 < 8) {
+              // Order: both scale bytes, then tile 0's operand, then tile 1's
+              // (the next pair's first MFMAs wait only for what they use).
+              if (j < 2) nxt[j].sc = A[a_sc + 64 * (2 * pp + 2 + j)];
+              const int t = 2 * pp + 2 + (j >= 4);
+              if (j == 2 || j == 4) nxt[j / 4].lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 2048 * t);
+              if (j == 3 || j == 5) nxt[j / 5].hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 2048 * t);
+            }
           }
-          // Keep this pair's MFMAs inside its condition, in this order (the
-          // compiler would otherwise sink them below the later pairs' reads).
+          // Keep this pair's MFMAs inside its condition (the compiler would
+          // otherwise sink them below the later pairs), interleaved with the
+          // reads.
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[2 * pp + h][i]));
+          if constexpr (pp + 1 < 8) {
+#pragma unroll
+            for (int q = 0; q < 6; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
       static_for<0, 8>(pair_fn);
     };
 
+    // Step s: MFMAs of stage s, weights of stage s + 3 into the set just
+    // used; then wait for stage s + 1's token rows (the loads issued after
+    // them are stage s + 1's weights and stages s + 2, s + 3: 42), barrier
+    // (stage s + 1 landed everywhere and stage s's buffer is free), read
+    // stage s + 1's first pair and fill stage s's buffer with stage s + 4.
     auto step = [&](WStage& cur, int s) __attribute__((always_inline)) {
-      // Token rows of stage s have landed for this wavefront; the barrier
-      // extends that to all wavefronts and tells that stage s - 1 is done
-      // everywhere, so its buffer can take stage s + 3.
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");
-      asm volatile("s_barrier" ::: "memory");
-      issue_act(s + 3);
-      asm volatile("" ::: "memory");
-      compute(cur, s);
+      compute(cur, stage_buf(s));
       asm volatile("" ::: "memory");
       load_w(cur, s + 3);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");
+      asm volatile("s_barrier" ::: "memory");
+      const lds_t* An = stage_buf(s + 1);
+      read_a(buf[0][0], An, 0);
+      read_a(buf[0][1], An, 1);
+      asm volatile("" ::: "memory");
+      issue_act(s + 4);
       asm volatile("" ::: "memory");
     };
     WStage w0, w1, w2;
@@ -280,6 +308,15 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     issue_act(2);
     asm volatile("" ::: "memory");
     load_w(w2, 2);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");   // stage 0's token rows
+    asm volatile("s_barrier" ::: "memory");
+    {
+      const lds_t* A0 = stage_buf(0);
+      read_a(buf[0][0], A0, 0);
+      read_a(buf[0][1], A0, 1);
+    }
+    asm volatile("" ::: "memory");
+    issue_act(3);
     asm volatile("" ::: "memory");
     // Stage loop, unrolled by 3 so each register set keeps a fixed name.
     int s = 0;
