@@ -17,16 +17,19 @@
 //   * weights go from memory straight to registers: one coalesced 16-byte
 //     load per lane per 16-row block and stage (in the tiled layout each
 //     block's MFMA operand is one contiguous 1 KB piece in lane order), three
-//     stages ahead in rotating register sets;
+//     stages ahead in four rotating register sets;
 //   * token rows go through a ring of 4 LDS stages (256 rows x 128 bytes +
 //     one scale dword per row), filled by direct buffer -> LDS loads three
 //     stages ahead; 16-byte chunks are XOR-swizzled by row bits 0..2 so the
-//     eight lanes served together hit eight bank groups.  Every wavefront
-//     issues the same loads per stage (9 direct-to-LDS, 8 to registers), so
-//     one fixed "s_waitcnt vmcnt" leaves exactly the later stages in flight;
-//     past the last stage the final stage is reloaded to keep that count;
+//     eight lanes served together hit eight bank groups;
 //   * token tiles are taken in pairs; pairs past the expert's last row are
-//     skipped (at most one empty 16-row tile is computed);
+//     skipped (at most one empty 16-row tile is computed).  Each of a pair's
+//     8 MFMAs is followed by one LDS read of the next pair and, on odd ones,
+//     one global load of stage s + 3, so reads and loads issue under the
+//     MFMAs rather than in bursts.  Every wavefront issues the same 17 loads
+//     per stage (9 direct-to-LDS, then 8 to registers), so one fixed
+//     "s_waitcnt vmcnt" per stage leaves exactly the later stages in flight;
+//     past the last stage the final stage is reloaded to keep that count;
 //   * buffer resources keep every per-lane address a 32-bit offset.
 #include "common.h"
 #include "fc_common.h"
@@ -52,11 +55,16 @@ constexpr int kNt = 2;                      // nontemporal policy for weight loa
 static_assert(kKS == kTileK && 2 * kBN == kTileRows, "tile shape");
 static_assert((16 << kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSizes, "tile prefix");
 
-// Loads issued per wavefront and stage; the wait for stage s leaves the
-// weights of stage s and both later stages in flight.
+// Loads issued per wavefront and stage: 9 direct-to-LDS (token rows and
+// their scales), then 8 to registers (weight blocks and scale bytes).  When
+// stage s is waited for (token rows and weights), the loads issued after it
+// are the next two stages': 2 * 17 = 34.
 constexpr int kActLoads = 9, kWLoads = 8;
-constexpr int kWaitCount = 3 * kWLoads + 2 * kActLoads;   // 42
+constexpr int kLoadsPerStage = kActLoads + kWLoads;
+constexpr int kWaitCount = 2 * kLoadsPerStage;   // 34
 static_assert(kWaitCount < 64, "vmcnt range");
+// First load of each tile pair's share (pair 7 issues none).
+constexpr int kLoadStart[9] = {0, 3, 6, 9, 11, 13, 15, 17, 17};
 
 // Raw buffer resource: base and byte size in SGPRs.  Sizes stay below 2^31,
 // so kOutOfRange (plus any stage offset) is always past the end.
@@ -186,25 +194,32 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
       as_voff = tok < rows_used ? (uint32_t)src * (K / 32) : kOutOfRange;
     }
 
-    auto issue_act = [&](int s) __attribute__((always_inline)) {
-      const int sc = min(s, n_stages - 1);
-      uint8_t* base = lds + (s % kNumBuf) * kStage;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + wave * 8192 + i * 1024, 16,
-                                                 a_voff[i], kKS * sc, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(acts_r, base + kABytes + wave * 256, 4, as_voff,
-                                               4 * sc, 0, 0);
-    };
-    auto load_w = [&](WStage& ws, int s) __attribute__((always_inline)) {
-      const int sc = min(s, n_stages - 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ws.w[i] = __builtin_bit_cast(
-            v4i, __builtin_amdgcn_raw_buffer_load_b128(w_r, w_voff, w_soff[i] + sc * w_step, kNt));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ws.s[i] = __builtin_amdgcn_raw_buffer_load_b8(ws_r, ws_voff, ws_soff[i] + sc * ws_step, 0);
+    // Load q (0..16) of stage s_load: q < 8 a 1 KB piece of token rows, q = 8
+    // the token scale dwords (direct to LDS, stage buffer s_load % 4); q < 13
+    // a weight block, q < 17 a weight scale byte (to register set ws).
+    auto issue_load = [&](int q, WStage& ws, int s_load) __attribute__((always_inline)) {
+      // Recomputed per load (cheap scalar work) rather than kept in scalar
+      // registers across the loop.
+      asm volatile("" : "+s"(s_load));
+      const int sc = min(s_load, n_stages - 1);
+      uint8_t* base = lds + (s_load % kNumBuf) * kStage;
+      if (q < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + wave * 8192 + q * 1024, 16,
+                                                 a_voff[q], kKS * sc, 0, 0);
+      else if (q == 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(acts_r, base + kABytes + wave * 256, 4, as_voff,
+                                                 4 * sc, 0, 0);
+      else if (q < 13)
+        // Weight loads are issued in assembly so that the compiler does not
+        // place its own (conservative) waits for them; the stage-end wait
+        // covers them and the registers are re-pinned after it.
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen nt"
+                     : "=v"(ws.w[q - 9])
+                     : "v"(w_voff), "s"(w_r), "s"(w_soff[q - 9] + sc * w_step));
+      else
+        asm volatile("buffer_load_ubyte %0, %1, %2, %3 offen"
+                     : "=v"(ws.s[q - 13])
+                     : "v"(ws_voff), "s"(ws_r), "s"(ws_soff[q - 13] + sc * ws_step));
     };
 
     v4f acc[16][4];  // [token tile][row block]
@@ -234,12 +249,18 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     };
 
     AOp buf[2][2];   // [pair parity][tile of the pair]
-    // One stage: pair pp's 8 MFMAs, each followed by one LDS read of pair
-    // pp + 1 (6 reads), so the reads hide under the MFMAs.  Pair 0's operands
-    // were read before the call.
-    auto compute = [&](const WStage& ws, const lds_t* A) __attribute__((always_inline)) {
+    // One stage.  Pair pp: 8 MFMAs; after MFMA j < 6 one LDS read of pair
+    // pp + 1, after MFMAs 1, 3, 5 the pair's share of the 17 global loads of
+    // stage s + 3 (token rows into the buffer stage s - 1 used, weights into
+    // register set nw), so neither the reads nor the loads stall the MFMAs.
+    // Skipped pairs still issue their loads: every stage issues the same 17,
+    // token rows (0..8) before weights (9..16).  Pair 0's operands were read
+    // before the call.
+    auto compute = [&](const WStage& ws, WStage& nw, int s) __attribute__((always_inline)) {
+      const lds_t* A = stage_buf(s);
       auto pair_fn = [&](auto ppi) __attribute__((always_inline)) {
         constexpr int pp = decltype(ppi)::value;
+        constexpr int q0 = kLoadStart[pp], q1 = kLoadStart[pp + 1];
         if (pp < npairs) {
           AOp(&cur)[2] = buf[pp & 1];
           AOp(&nxt)[2] = buf[(pp + 1) & 1];
@@ -249,84 +270,86 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
             acc[2 * pp + h][i] =
                 mfma_w4a8<0>(ws.w[i], cur[h].lo, cur[h].hi, acc[2 * pp + h][i], ws.s[i], cur[h].sc);
             if constexpr (pp + 1 < 8) {
-              // Order: both scale bytes, then tile 0's operand, then tile 1's
-              // (the next pair's first MFMAs wait only for what they use).
+              // Both scale bytes, then tile 0's operand, then tile 1's (the
+              // next pair's first MFMAs wait only for what they use).
               if (j < 2) nxt[j].sc = A[a_sc + 64 * (2 * pp + 2 + j)];
               const int t = 2 * pp + 2 + (j >= 4);
               if (j == 2 || j == 4) nxt[j / 4].lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 2048 * t);
               if (j == 3 || j == 5) nxt[j / 5].hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 2048 * t);
             }
+            if ((j & 1) && q0 + (j >> 1) < q1) issue_load(q0 + (j >> 1), nw, s + 3);
           }
           // Keep this pair's MFMAs inside its condition (the compiler would
-          // otherwise sink them below the later pairs), interleaved with the
-          // reads.
+          // otherwise sink them below the later pairs), in the order above.
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[2 * pp + h][i]));
-          if constexpr (pp + 1 < 8) {
 #pragma unroll
-            for (int q = 0; q < 6; ++q) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+            if (pp + 1 < 8 && j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            if ((j & 1) && q0 + (j >> 1) < q1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
+        } else {
+#pragma unroll
+          for (int q = q0; q < q1; ++q) issue_load(q, nw, s + 3);
         }
       };
       static_for<0, 8>(pair_fn);
     };
 
-    // Step s: MFMAs of stage s, weights of stage s + 3 into the set just
-    // used; then wait for stage s + 1's token rows (the loads issued after
-    // them are stage s + 1's weights and stages s + 2, s + 3: 42), barrier
-    // (stage s + 1 landed everywhere and stage s's buffer is free), read
-    // stage s + 1's first pair and fill stage s's buffer with stage s + 4.
-    auto step = [&](WStage& cur, int s) __attribute__((always_inline)) {
-      compute(cur, stage_buf(s));
-      asm volatile("" ::: "memory");
-      load_w(cur, s + 3);
+    // After the stage-end wait the next stage's weights are in their
+    // registers: re-define them there so no use can move above the wait.
+    auto pin_w = [&](WStage& w) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(w.w[i]), "+v"(w.s[i]));
+    };
+    // Step s (set cur holds stage s's weights, nw takes stage s + 3's, next
+    // holds stage s + 1's): the stage's MFMAs and loads, then the wait for
+    // stage s + 1 (its 17 loads were issued two steps back, followed by the 17
+    // of each later step: 34), the barrier (stage s + 1 landed everywhere,
+    // stage s's buffer free), stage s + 1's first pair.
+    auto step = [&](const WStage& cur, WStage& nw, WStage& next, int s) __attribute__((always_inline)) {
+      compute(cur, nw, s);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");
       asm volatile("s_barrier" ::: "memory");
+      pin_w(next);
       const lds_t* An = stage_buf(s + 1);
       read_a(buf[0][0], An, 0);
       read_a(buf[0][1], An, 1);
       asm volatile("" ::: "memory");
-      issue_act(s + 4);
-      asm volatile("" ::: "memory");
     };
-    WStage w0, w1, w2;
-    issue_act(0);
+    WStage w0, w1, w2, w3;
+#pragma unroll
+    for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, w0, 0);
     asm volatile("" ::: "memory");
-    load_w(w0, 0);
+#pragma unroll
+    for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, w1, 1);
     asm volatile("" ::: "memory");
-    issue_act(1);
-    asm volatile("" ::: "memory");
-    load_w(w1, 1);
-    asm volatile("" ::: "memory");
-    issue_act(2);
-    asm volatile("" ::: "memory");
-    load_w(w2, 2);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");   // stage 0's token rows
+#pragma unroll
+    for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, w2, 2);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");   // stage 0's loads
     asm volatile("s_barrier" ::: "memory");
+    pin_w(w0);
     {
       const lds_t* A0 = stage_buf(0);
       read_a(buf[0][0], A0, 0);
       read_a(buf[0][1], A0, 1);
     }
     asm volatile("" ::: "memory");
-    issue_act(3);
-    asm volatile("" ::: "memory");
-    // Stage loop, unrolled by 3 so each register set keeps a fixed name.
+    // Stage loop, unrolled by 4 so each register set keeps a fixed name.
     int s = 0;
-    for (; s + 3 <= n_stages; s += 3) {
-      step(w0, s);
-      step(w1, s + 1);
-      step(w2, s + 2);
+    for (; s + 4 <= n_stages; s += 4) {
+      step(w0, w3, w1, s);
+      step(w1, w0, w2, s + 1);
+      step(w2, w1, w3, s + 2);
+      step(w3, w2, w0, s + 3);
     }
-    if (s < n_stages) step(w0, s);
-    if (s + 1 < n_stages) step(w1, s + 1);
+    if (s < n_stages) step(w0, w3, w1, s);
+    if (s + 1 < n_stages) step(w1, w0, w2, s + 1);
+    if (s + 2 < n_stages) step(w2, w1, w3, s + 2);
     // Drain the reloads issued past the end before the ring is reused.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
