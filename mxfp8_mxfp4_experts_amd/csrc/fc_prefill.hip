@@ -350,8 +350,15 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     if (s < n_stages) step(w0, w3, w1, s);
     if (s + 1 < n_stages) step(w1, w0, w2, s + 1);
     if (s + 2 < n_stages) step(w2, w1, w3, s + 2);
-    // Drain the reloads issued past the end before the ring is reused.
+    // Drain the reloads issued past the end before the ring is reused.  The
+    // weight loads are asynchronous writes the compiler does not see: keep
+    // every register set allocated until they have landed, so none of them
+    // is handed to another value while a load into it is in flight.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    pin_w(w0);
+    pin_w(w1);
+    pin_w(w2);
+    pin_w(w3);
     asm volatile("s_barrier" ::: "memory");
 
     auto pin = [&](auto tti) __attribute__((always_inline)) {
