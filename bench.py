@@ -25,8 +25,15 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense MXFP8-rate scaled MFMA (f8 x f4 issues at this rate)
 
 WORKLOADS = {"tiny": 0, "decode_T8": 1, "batched_decode_T256": 2, "prefill_T8192": 3,
-             "ep_share_T4096": 4}
+             "ep_share_T4096": 4, "ckpt_ep32r7_M128": 5, "ckpt_ep32r7_M512": 6,
+             "ckpt_ep32r7_M2048": 7, "ckpt_ep32r7_M8192": 8}
 
+
+# The pages' own latency for the checkpoint-true "ep_mixed" runner workload
+# (FlashInfer CUTLASS MXFP8 x MXFP4, SiTU(4, 25), RTX PRO 6000D / SM120;
+# page 1, "Phase 4 算子性能与 Profiler 归因", "五轮交错 A/B" table): local batch M
+# -> median ms.  Another machine's figure: context for vs_baseline.
+PAGES_EP_MIXED_MS = {128: 0.926, 512: 1.782, 2048: 4.355, 8192: 16.167}
 
 # Sources of the FC kernels: a traffic figure is valid only for these bytes.
 FC_SOURCES = ("common.h", "fc_common.h", "tiled.h", "fc.hip", "fc_prefill.hip")
@@ -119,12 +126,17 @@ def main():
         w_all = synth.make_expert_weights(wcfg, device=dev)
         sl = slice(cfg.expert_offset, cfg.expert_offset + cfg.E_local)
         w = {k: v[sl] for k, v in w_all.items()}
+    elif cfg.routing == "ep_mixed":
+        w = synth.make_expert_weights(cfg, device=dev)
     else:
         w = {k: v.to(dev) for k, v in synth.make_expert_weights(cfg, device="cpu").items()}
     act = synth.make_activations(cfg)
     x = torch.from_numpy(act["x_bf16"].astype(np.int16)).to(dev).view(torch.bfloat16)
-    logits = torch.from_numpy(act["logits"]).to(dev)
-    bias = torch.from_numpy(act["bias"]).to(dev)
+    # "ep_mixed" workloads take their top-k ids and weights as inputs (the
+    # pages' harness does the same); the others route from the logits.
+    given = cfg.routing == "ep_mixed"
+    logits = None if given else torch.from_numpy(act["logits"]).to(dev)
+    bias = None if given else torch.from_numpy(act["bias"]).to(dev)
     layer = m.MoELayer(w["w13"], w["w13_s"], w["w2"], w["w2_s"], top_k=cfg.K, E=cfg.E,
                        expert_offset=cfg.expert_offset, routed_scaling=cfg.routed_scaling,
                        situ_alpha=cfg.situ_alpha, situ_beta=cfg.situ_beta, max_tokens=cfg.T)
@@ -137,12 +149,16 @@ def main():
     K, T, H, I, E_local = cfg.K, cfg.T, cfg.H, cfg.I, cfg.E_local
     R = T * K
     idx, tw = layer.topk_idx[:T], layer.topk_w[:T]
+    if given:
+        idx.copy_(torch.from_numpy(act["topk_idx"]))
+        tw.copy_(torch.from_numpy(act["topk_w"]))
     xq, xs = layer.xq[:T], layer.xs[:T]
     sroute, rrow = layer.sorted_route[:R], layer.route_row[:R]
     hq, hs = layer.hq[:R], layer.hs[:R]
 
     def step(ev=None):
-        B.moe_route(logits, bias, K, cfg.routed_scaling, idx, tw)
+        if not given:
+            B.moe_route(logits, bias, K, cfg.routed_scaling, idx, tw)
         B.moe_quant_mxfp8(x, xq, xs)
         B.moe_permute(idx, cfg.expert_offset, E_local, layer.workspace, layer.expert_offsets,
                       sroute, rrow)
@@ -174,7 +190,8 @@ def main():
     fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
     # The timed calls must compute what the layer computes.
-    ref = layer(x, logits, bias)
+    ref = layer(x, logits, bias, topk_idx=idx.clone() if given else None,
+                topk_w=tw.clone() if given else None)
     if not torch.equal(ref.view(torch.int16), out.view(torch.int16)):
         print("[bench] timed path disagrees with MoELayer", file=sys.stderr, flush=True)
         sys.exit(1)
@@ -188,7 +205,8 @@ def main():
     w13_bytes = 2 * I * H * (1 / 2 + 1 / 32)
     fc1_bytes = D * w13_bytes + tokens_used * H * (1 + 1 / 32) + n_kept * I * (1 + 1 / 32)
     fc1_flops = 2.0 * n_kept * 2 * I * H
-    layer_bytes = (D * H * I * 1.59375 + 2 * T * H + 4 * T * cfg.E + 2 * 1.03125 * T * H
+    layer_bytes = (D * H * I * 1.59375 + 2 * T * H + (0 if given else 4 * T * cfg.E)
+                   + 2 * 1.03125 * T * H
                    + 2 * 1.03125 * n_kept * I + 2 * T * H)
     layer_flops = n_kept * 6.0 * H * I
     traffic = _traffic(args.workload)
@@ -221,12 +239,16 @@ def main():
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": None,
+        "vs_baseline": (round(T / (ms_per_step * 1e-3) / (T / (PAGES_EP_MIXED_MS[T] * 1e-3)), 4)
+                        if given and T in PAGES_EP_MIXED_MS else None),
         "dtype": "e4m3xe2m1_f32acc",
-        "data": "synthetic (seeded; x~N(0,1) bf16, weights N(0,0.02) -> MXFP4)",
+        "data": "synthetic (seeded; x~N(0,1) bf16, weights N(0,0.02) -> MXFP4"
+                + ("; top-k ids/weights given: 8 local + 8 remote slots per token)" if given
+                   else "; router logits N(0,1), bias per workload)"),
         "config": {"workload": f"kimi_k3_moe_{args.workload}", "T": T, "H": H, "I": I,
                    "E": cfg.E, "top_k": K, "E_local": E_local,
-                   "expert_offset": cfg.expert_offset, "experts_touched": D,
+                   "expert_offset": cfg.expert_offset, "routing": cfg.routing,
+                   "experts_touched": D,
                    "routed_rows": n_kept},
         "layer": {"hbm_frac": round(layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(layer_flops / (ms_per_step * 1e-3) / 1e12

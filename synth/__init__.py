@@ -17,6 +17,15 @@ Recipe (one seeded scheme for every workload):
 * correction bias: ``0.1 * standard_normal(float32)`` ``[E]``, or for the
   skewed expert-parallel share ``0.04 * ln(r ** -1.2)`` with ``r`` a seeded
   permutation of ``1..E`` (a Zipf(1.2) popularity folded into the bias);
+* "ep_mixed" workloads (the checkpoint-true expert shape of page 1, "真实
+  checkpoint 契约": routed latent 3584, expert intermediate 3072, 28 local
+  experts of 896 on rank 7 of 32, and its benchmark, where 8 of each token's
+  16 slots name local experts and 8 remote ones) take their top-k ids and
+  weights from the generator instead of the router: per token, 8 distinct
+  local ids and 8 distinct remote ids (uniform, without replacement, from
+  the ``bias`` stream), the 16 slots in a seeded random order (``perm``
+  stream), weights ``sigmoid(z)`` with ``z ~ N(0, 1)`` (``logits`` stream)
+  normalised to sum 1 over the token's slots;
 * expert weights: per-expert torch generator seeded from
   ``spawn_key=(99, e)``; ``0.02 * randn`` rounded to bf16, then MXFP4 with the
   smallest power-of-two scale that keeps the group's absmax within 6 and
@@ -50,6 +59,7 @@ class LayerConfig:
     E_local: int      # experts held by this GPU
     expert_offset: int = 0
     bias_kind: str = "normal"   # "normal" | "zipf" | "zero"
+    routing: str = "router"     # "router" (a1 on the logits) | "ep_mixed" (given top-k)
     routed_scaling: float = 1.0
     situ_alpha: float = 4.0
     situ_beta: float = 25.0
@@ -69,6 +79,12 @@ CONFIGS = {
     4: LayerConfig("ep_share_T4096", 4, T=4096, H=7168, I=3584, E=896, K=16, E_local=224,
                    expert_offset=0, bias_kind="zipf"),
 }
+# The checkpoint-true expert shape with the pages' own benchmark routing (one
+# GPU of 32 holding experts [196, 224), 8 local + 8 remote slots per token),
+# at the four local batch sizes the pages measure.
+for _i, _m in enumerate((128, 512, 2048, 8192)):
+    CONFIGS[5 + _i] = LayerConfig(f"ckpt_ep32r7_M{_m}", 5 + _i, T=_m, H=3584, I=3072, E=896,
+                                  K=16, E_local=28, expert_offset=196, routing="ep_mixed")
 
 
 def custom_config(name: str, key: int, **kw) -> LayerConfig:
@@ -95,13 +111,36 @@ def _streams(cfg: LayerConfig, seed: int):
     return [np.random.default_rng(s) for s in ss.spawn(4)]
 
 
+def make_topk_ep_mixed(cfg: LayerConfig, T: int, r_w, r_ids, r_order):
+    """Top-k ids and weights of an "ep_mixed" workload: 8 local and 8 remote
+    distinct experts per token (K = 16), slots shuffled, positive weights
+    summing to 1 per token."""
+    assert cfg.K == 16 and cfg.E_local >= 8 and cfg.E - cfg.E_local >= 8
+    n_loc = cfg.K // 2
+    loc = np.argsort(r_ids.random((T, cfg.E_local)), axis=1)[:, :n_loc] + cfg.expert_offset
+    rem = np.argsort(r_ids.random((T, cfg.E - cfg.E_local)), axis=1)[:, :cfg.K - n_loc]
+    rem = np.where(rem < cfg.expert_offset, rem, rem + cfg.E_local)
+    ids = np.concatenate([loc, rem], axis=1)
+    order = np.argsort(r_order.random((T, cfg.K)), axis=1)
+    ids = np.take_along_axis(ids, order, axis=1).astype(np.int32)
+    s = 1.0 / (1.0 + np.exp(-r_w.standard_normal((T, cfg.K))))
+    w = (s / s.sum(axis=1, keepdims=True)).astype(np.float32)
+    return ids, w
+
+
 def make_activations(cfg: LayerConfig, seed: int = ROOT_SEED, T: Optional[int] = None):
-    """Return dict(x_bf16 uint16[T,H], logits f32[T,E], bias f32[E]).
+    """Return dict(x_bf16 uint16[T,H], logits f32[T,E], bias f32[E]); for
+    "ep_mixed" workloads dict(x_bf16, topk_idx int32[T,K], topk_w f32[T,K])
+    instead of the router inputs.
 
     ``T`` may shorten the token count (the first rows of the same streams are
     NOT reproduced; a shorter draw is its own case)."""
     T = cfg.T if T is None else T
     r_logits, r_bias, r_x, r_perm = _streams(cfg, seed)
+    if cfg.routing == "ep_mixed":
+        ids, w = make_topk_ep_mixed(cfg, T, r_logits, r_bias, r_perm)
+        x = f32_to_bf16_bits(r_x.standard_normal((T, cfg.H), dtype=np.float32))
+        return {"x_bf16": x, "topk_idx": ids, "topk_w": w}
     logits = r_logits.standard_normal((T, cfg.E), dtype=np.float32)
     if cfg.bias_kind == "normal":
         bias = (np.float32(0.1) * r_bias.standard_normal(cfg.E, dtype=np.float32)).astype(np.float32)

@@ -384,3 +384,74 @@ def test_full_size_sampled(cid, tiled):
                            lambda e: mxfp4_dequantize(to_np(w_dev["w2"][e]), to_np(w_dev["w2_s"][e])),
                            cfg.H)
     assert_output_with_allowance(res["out"][toks], sub["out"], allow, f"full c{cid}")
+
+
+# ---------------------------------------------------------------------------
+# The checkpoint-true expert shape with the pages' own benchmark routing
+# (28 local experts of 896, 8 local + 8 remote slots per token): top-k ids
+# and weights are inputs here, as in the pages' harness.
+
+_CKPT_W = {}
+
+
+def _ckpt_weights(cfg):
+    if "w" not in _CKPT_W:
+        _CKPT_W["w"] = synth.make_expert_weights(cfg, device=DEV)
+    return _CKPT_W["w"]
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+def test_ckpt_shape_M128_all_tokens(tiled):
+    cfg = synth.CONFIGS[5]
+    print(f"[ckpt M128 tiled={tiled}] {cfg}", flush=True)
+    act = synth.make_activations(cfg)
+    w_dev = _ckpt_weights(cfg)
+    w_np = {k: to_np(v) for k, v in w_dev.items()}
+    layer = _layer_for(cfg, w_dev, cfg.T, tiled=tiled)
+    x = torch.from_numpy(act["x_bf16"].astype(np.int16)).to(DEV).view(torch.bfloat16)
+    res = run_steps(layer, x, None, None, torch.from_numpy(act["topk_idx"]).to(DEV),
+                    torch.from_numpy(act["topk_w"]).to(DEV))
+    ref = oracle.oracle_layer(act["x_bf16"], None, None, w_np["w13"], w_np["w13_s"], w_np["w2"],
+                              w_np["w2_s"], top_k=cfg.K, expert_offset=cfg.expert_offset,
+                              topk_idx=act["topk_idx"], topk_w=act["topk_w"])
+    _check_full(cfg, act, res, ref, f"ckpt M128 tiled={tiled}", w_np)
+
+
+@pytest.mark.parametrize("cid", [7, 8])
+def test_ckpt_shape_large_M_sampled(cid):
+    cfg = synth.CONFIGS[cid]
+    print(f"[ckpt c{cid}] {cfg}", flush=True)
+    act = synth.make_activations(cfg)
+    w_dev = _ckpt_weights(cfg)
+    layer = _layer_for(cfg, w_dev, cfg.T)
+    x = torch.from_numpy(act["x_bf16"].astype(np.int16)).to(DEV).view(torch.bfloat16)
+    rid, rw = act["topk_idx"], act["topk_w"]
+    res = run_steps(layer, x, None, None, torch.from_numpy(rid).to(DEV), torch.from_numpy(rw).to(DEV))
+    rows = np.random.default_rng(2).choice(cfg.T, 1024, replace=False)
+    rq, rs = oracle.quant_x(act["x_bf16"][rows])
+    assert np.array_equal(res["xq"][rows], rq) and np.array_equal(res["xs"][rows], rs)
+    offs, sroute, rrow = oracle.permute(rid, cfg.expert_offset, cfg.E_local)
+    assert np.array_equal(res["expert_offsets"], offs)
+    assert np.array_equal(res["sorted_route"][:offs[-1]], sroute)
+    assert np.array_equal(res["route_row"], rrow)
+    toks = _sample_tokens(rid, cfg, 3)
+
+    def weight_fn(e):
+        return tuple(to_np(w_dev[k][e]) for k in ("w13", "w13_s", "w2", "w2_s"))
+
+    sub = oracle.oracle_tokens(toks, act["x_bf16"], rid, rw, weight_fn, top_k=cfg.K,
+                               expert_offset=cfg.expert_offset, E_local=cfg.E_local)
+    mism, deltas = [], {}
+    for (j, k), (hq_ref, hs_ref, a_ref) in sub["h"].items():
+        row = int(rrow[toks[j] * cfg.K + k])
+        mism.append(byte_mismatch(res["hq"][row], hq_ref))
+        deltas[row] = check_requant(res["hq"][row:row + 1], res["hs"][row:row + 1], a_ref[None],
+                                    hq_ref[None], hs_ref[None], f"ckpt c{cid} row {row}",
+                                    max_frac=5e-3)[0]
+    print(f"[ckpt c{cid}] tokens {toks}: mean hq mismatch {np.mean(mism):.3g}", flush=True)
+    assert np.mean(mism) <= 1e-3
+    allow = flip_allowance(lambda row: deltas.get(row), toks, cfg.K, rrow, rw,
+                           lambda row: np.searchsorted(offs, row, side="right") - 1,
+                           lambda e: mxfp4_dequantize(to_np(w_dev["w2"][e]), to_np(w_dev["w2_s"][e])),
+                           cfg.H)
+    assert_output_with_allowance(res["out"][toks], sub["out"], allow, f"ckpt c{cid}")

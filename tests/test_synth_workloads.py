@@ -1,0 +1,53 @@
+"""The seeded workloads reproduce the shapes and routing structure the pages
+state for their own benchmark (facts in tests/golden/kimi_k3_facts.json)."""
+import json
+import os
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "kimi_k3_facts.json")
+
+
+def _facts():
+    return json.load(open(GOLDEN))
+
+
+def test_ep_mixed_configs_match_the_pages_benchmark():
+    f = _facts()["ep_mixed_benchmark"]
+    ck = _facts()["ep_mapping"]
+    cfgs = [c for c in synth.CONFIGS.values() if c.routing == "ep_mixed"]
+    assert [c.T for c in cfgs] == f["M"]
+    for c in cfgs:
+        assert (c.H, c.I, c.E, c.E_local, c.K) == (f["H"], f["I"], f["E"], f["E_local"], f["top_k"])
+        assert c.E_local == ck["num_global"] // ck["ep"]
+        assert c.expert_offset == f["ep_rank"] * c.E_local
+
+
+def test_ep_mixed_routing_structure():
+    f = _facts()["ep_mixed_benchmark"]
+    for c, avg in zip([c for c in synth.CONFIGS.values() if c.routing == "ep_mixed"][:2],
+                      f["avg_local_routes_per_expert"]):
+        a = synth.make_activations(c)
+        ids, w = a["topk_idx"], a["topk_w"]
+        assert ids.shape == (c.T, c.K) and ids.dtype == np.int32 and w.dtype == np.float32
+        local = (ids >= c.expert_offset) & (ids < c.expert_offset + c.E_local)
+        assert np.all(local.sum(1) == f["local_slots"])
+        assert all(len(set(row)) == c.K for row in ids)           # distinct experts per token
+        assert ids.min() >= 0 and ids.max() < c.E
+        assert np.all(w > 0) and np.allclose(w.sum(1), 1.0, atol=1e-6)
+        per_expert = np.bincount(ids[local] - c.expert_offset, minlength=c.E_local)
+        assert abs(per_expert.mean() - avg) < 0.05                # M * 8 / 28, as printed
+
+
+def test_checkpoint_true_weight_shapes():
+    """w13 = [w1; w3] and w2 of the local window have the checkpoint's shapes."""
+    t = _facts()["checkpoint_expert_tensors"]
+    c = synth.CONFIGS[5]
+    small = synth.custom_config("shape", 0, T=1, H=c.H, I=c.I, E=c.E, K=1, E_local=1)
+    w = synth.make_expert_weights(small, experts=[c.expert_offset])
+    assert tuple(w["w13"].shape[1:]) == (2 * t["w1.weight_packed"][0], t["w1.weight_packed"][1])
+    assert tuple(w["w13_s"].shape[1:]) == (2 * t["w1.weight_scale"][0], t["w1.weight_scale"][1])
+    assert tuple(w["w2"].shape[1:]) == tuple(t["w2.weight_packed"])
+    assert tuple(w["w2_s"].shape[1:]) == tuple(t["w2.weight_scale"])
