@@ -39,20 +39,45 @@ struct FcParams {
 
 // SiTU(g, u) = alpha tanh(g / alpha) sigmoid(g) * beta tanh(u / beta)
 // (page 1, "真实 checkpoint 契约": the SiTU activation with alpha = 4, beta =
-// 25), from the hardware base-2 exponential and reciprocal:
-//   sigmoid(g) = 1 / (1 + 2^(-g log2 e)),  tanh(y) = 1 - 2 / (1 + 2^(2 y log2 e)).
-// Each factor is within a few float32 ulps of its value (the tanh form loses
-// only absolute accuracy, ~1e-7, for small |y|), far below the E4M3 rounding
-// the result goes through next.  Infinite exponentials give the limits
-// (tanh -> +-1, sigmoid -> 0 or 1); NaN propagates.
+// 25; alpha, beta > 0), from three hardware base-2 exponentials and one
+// reciprocal.  With z1 = e^(-2g/alpha), z2 = e^(-g), w = e^(-2u/beta):
+//   tanh(g/alpha) = (1 - z1) / (1 + z1),  sigmoid(g) = 1 / (1 + z2),
+//   tanh(u/beta) = (1 - w) / (1 + w),
+// so SiTU = alpha beta (1 - z1)(1 - w) / ((1 + z1)(1 + z2)(1 + w)).  The
+// numerators take the sign of g and u (tanh keeps the sign of zero).  Each
+// exponent is capped at e^40: the numerator stays finite, and where the
+// denominator overflows the true value is below 1e-16 and the result is a
+// signed zero.  Accuracy: a few float32 ulps relative, ~1e-7 absolute near
+// zero, far inside the E4M3 step the result goes through next.  A NaN input
+// gives 0 here (the requantisation rule sends NaN to code 0 and leaves it
+// out of the block maximum, which is what 0 does).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float fast_tanh(float y) {
-  return 1.0f - 2.0f * fast_rcp(1.0f + fast_exp2(y * 2.8853900817779268f));   // 2 log2 e
+struct SituConst {
+  float k1, k2, k3, ab;   // -2 log2(e) / alpha, -log2(e), -2 log2(e) / beta, alpha beta
+};
+__device__ __forceinline__ SituConst situ_const(float alpha, float beta) {
+  const float l2e = 1.4426950408889634f;
+  return SituConst{-2.0f * l2e / alpha, -l2e, -2.0f * l2e / beta, alpha * beta};
 }
-__device__ __forceinline__ float situ(float g, float u, float alpha, float beta) {
-  const float sig = fast_rcp(1.0f + fast_exp2(g * -1.4426950408889634f));     // -log2 e
-  return alpha * fast_tanh(g * fast_rcp(alpha)) * sig * (beta * fast_tanh(u * fast_rcp(beta)));
+__device__ __forceinline__ float situ(float g, float u, const SituConst& c) {
+  const float cap = 57.70780163555853f;   // 40 log2(e)
+  const float z1 = fast_exp2(fminf(g * c.k1, cap));
+  const float z2 = fast_exp2(fminf(g * c.k2, cap));
+  const float w = fast_exp2(fminf(u * c.k3, cap));
+  const float num = copysignf(1.0f - z1, g) * copysignf(1.0f - w, u);
+  const float den = (1.0f + z1) * (1.0f + z2) * (1.0f + w);
+  const float v = c.ab * num * fast_rcp(den);
+  return __builtin_isunordered(g, u) ? 0.0f : v;
+}
+// Four E4M3 codes of x / s (s a normal power of two, |x / s| <= 448), packed
+// little-endian, by the hardware scaled conversion.
+typedef short v2s __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3x4_scaled(float x0, float x1, float x2, float x3,
+                                                  float s) {
+  v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x0, x1, s, false);
+  v2s both = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x2, x3, s, true);
+  return __builtin_bit_cast(uint32_t, both);
 }
 
 // Largest expert e with prefix[e] <= tile (the expert owning that tile).
@@ -94,11 +119,12 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
                                               bool valid, int u, int g) {
   if (FC1) {
     const int c0 = u * 32;
+    const SituConst sc = situ_const(p.alpha, p.beta);
     float a[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      a[r] = situ(acc[0][r], acc[2][r], p.alpha, p.beta);       // column c0 + 4g + r
-      a[4 + r] = situ(acc[1][r], acc[3][r], p.alpha, p.beta);   // column c0 + 16 + 4g + r
+      a[r] = situ(acc[0][r], acc[2][r], sc);       // column c0 + 4g + r
+      a[4 + r] = situ(acc[1][r], acc[3][r], sc);   // column c0 + 16 + 4g + r
     }
     float amax = 0.0f;
 #pragma unroll
@@ -110,10 +136,19 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const int ex = mx8_exponent(amax);
     uint32_t q0 = 0, q1 = 0;
+    if (ex > -127) {
+      // gfx950's scaled conversion divides by the power of two 2^ex and
+      // rounds to the nearest E4M3 (ties to even) -- the same code as
+      // e4m3_encode for every |value| <= 448, which the scale guarantees.
+      const float s2 = __uint_as_float((uint32_t)(ex + 127) << 23);
+      q0 = e4m3x4_scaled(a[0], a[1], a[2], a[3], s2);
+      q1 = e4m3x4_scaled(a[4], a[5], a[6], a[7], s2);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      q0 |= e4m3_encode(ldexpf(a[r], -ex)) << (8 * r);
-      q1 |= e4m3_encode(ldexpf(a[4 + r], -ex)) << (8 * r);
+      for (int r = 0; r < 4; ++r) {
+        q0 |= e4m3_encode(ldexpf(a[r], -ex)) << (8 * r);
+        q1 |= e4m3_encode(ldexpf(a[4 + r], -ex)) << (8 * r);
+      }
     }
     if (valid) {
       uint8_t* dst = p.hq + (size_t)row * p.I + c0 + 4 * g;
