@@ -19,10 +19,16 @@ constexpr int kNumTileSizes = 5;
 
 // ---------------------------------------------------------------------------
 // Workspace layout shared by moe_permute / moe_fc1_situ / moe_fc2_combine.
-// Routes per chunk of the multi-workgroup grouping (moe_permute on large
-// batches): one wavefront ranks one chunk.
-constexpr int kPermChunk = 2048;
-inline int perm_chunks(int64_t R) { return (int)((R + kPermChunk - 1) / kPermChunk); }
+// Grouping (moe_permute): batches of at most kPermSingle routes take one
+// workgroup; larger ones are cut into chunks, one wavefront ranking each --
+// 256 routes per chunk up to 16384 routes (enough chunks to spread the
+// ranking), 2048 above (few enough that the per-expert scan over chunks
+// stays short).
+constexpr int kPermSingle = 2048;
+__host__ __device__ inline int perm_chunk_size(int64_t R) { return R <= 16384 ? 256 : 2048; }
+inline int perm_chunks(int64_t R) {
+  return R <= kPermSingle ? 0 : (int)((R + perm_chunk_size(R) - 1) / perm_chunk_size(R));
+}
 
 struct WsLayout {
   size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1]

@@ -235,16 +235,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   if (gid >= (int64_t)T * per_row) return;
   const int t = (int)(gid / per_row), c = (int)(gid % per_row);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < K; ++k) {
-    const int rr = route_row[(size_t)t * K + k];
-    if (rr < 0) continue;
-    const float wk = topk_w[(size_t)t * K + k];
-    const v4f* src = reinterpret_cast<const v4f*>(y + (size_t)rr * H + (size_t)c * 8);
-    const v4f a = src[0], b2 = src[1];
+  // Slots in groups of 16: all route rows and weights of the group first,
+  // then all row loads (independent, in flight together), then the sums in
+  // slot order.
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    int rr[16];
+    float wk[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] = fmaf(wk, a[i], acc[i]);
-      acc[4 + i] = fmaf(wk, b2[i], acc[4 + i]);
+    for (int j = 0; j < 16; ++j) {
+      const int k = k0 + j;
+      rr[j] = k < K ? route_row[(size_t)t * K + k] : -1;
+      wk[j] = k < K ? topk_w[(size_t)t * K + k] : 0.0f;
+    }
+    v4f a[16], b[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      a[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      b[j] = a[j];
+      if (rr[j] >= 0) {
+        const v4f* src = reinterpret_cast<const v4f*>(y + (size_t)rr[j] * H + (size_t)c * 8);
+        a[j] = src[0];
+        b[j] = src[1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (rr[j] < 0) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = fmaf(wk[j], a[j][i], acc[i]);
+        acc[4 + i] = fmaf(wk[j], b[j][i], acc[4 + i]);
+      }
     }
   }
   uint4 o;

@@ -10,7 +10,7 @@ hipError_t launch_route(const float* logits, int64_t ld, const float* bias, int 
                         float scaling, int32_t* idx, float* w, hipStream_t stream);
 hipError_t launch_quant(const uint16_t* x, int64_t ld, int T, int H, uint8_t* xq, uint8_t* xs,
                         hipStream_t stream);
-// counts: int32 [perm_chunks(R)][E_local] scratch (used when R > kPermChunk).
+// counts: int32 [perm_chunks(R)][E_local] scratch (used when R > kPermSingle).
 hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, int32_t* offs,
                           int32_t* sorted_route, int32_t* route_row, int32_t* tile_prefix,
                           int32_t* counts, hipStream_t stream);

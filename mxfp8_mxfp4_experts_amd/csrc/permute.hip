@@ -18,7 +18,7 @@
 //     bits, the lowest such lane reserves their rows from the expert's LDS
 //     cursor, and each lane takes base + its rank among them.  This keeps
 //     the (token, slot) order inside every expert.
-// Large batches: the routes are cut into chunks of kPermChunk; a count
+// Large batches: the routes are cut into chunks (perm_chunk_size); a count
 // kernel writes each chunk's histogram, one workgroup turns the histograms
 // into expert offsets, tile prefixes and each chunk's first row per expert,
 // and a rank kernel (one wavefront per chunk) runs step 3 on its chunk from
@@ -163,14 +163,14 @@ __device__ __forceinline__ int local_expert(const int32_t* idx, int r, int R, in
 
 // Histogram of one chunk's local expert ids.
 __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restrict__ idx, int R,
-                                                         int offset, int E_local,
+                                                         int offset, int E_local, int chunk,
                                                          int32_t* __restrict__ counts) {
   extern __shared__ int cnt_s[];
   const int c = blockIdx.x;
   for (int e = threadIdx.x; e < E_local; e += 256) cnt_s[e] = 0;
   __syncthreads();
-  const int r0 = c * kPermChunk;
-  for (int r = r0 + threadIdx.x; r < r0 + kPermChunk; r += 256) {
+  const int r0 = c * chunk;
+  for (int r = r0 + threadIdx.x; r < r0 + chunk; r += 256) {
     const int l = local_expert(idx, r, R, offset, E_local);
     if (l >= 0) atomicAdd(&cnt_s[l], 1);
   }
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
 
 // Step 3 on one chunk, from the chunk's starting rows.
 __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ idx, int R,
-                                                       int offset, int E_local,
+                                                       int offset, int E_local, int chunk,
                                                        const int32_t* __restrict__ starts,
                                                        int32_t* __restrict__ sorted_route,
                                                        int32_t* __restrict__ route_row) {
@@ -264,8 +264,8 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E_local) ++nbits;
-  const int r0 = c * kPermChunk;
-  const int r_end = min(r0 + kPermChunk, R);
+  const int r0 = c * chunk;
+  const int r_end = min(r0 + chunk, R);
   for (int base = r0; base < r_end; base += 64) {
     const int r = base + lane;
     const int l = local_expert(idx, r, r_end, offset, E_local);
@@ -302,20 +302,20 @@ __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict
 hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, int32_t* offs,
                           int32_t* sorted_route, int32_t* route_row, int32_t* tile_prefix,
                           int32_t* counts, hipStream_t stream) {
-  if (R <= kPermChunk) {
+  if (R <= kPermSingle) {
     const size_t lds = sizeof(int) * 2 * (size_t)E_local;
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, stream, idx, R, offset,
                        E_local, offs, sorted_route, route_row, tile_prefix);
     return hipGetLastError();
   }
-  const int n_chunks = perm_chunks(R);
+  const int n_chunks = perm_chunks(R), chunk = perm_chunk_size(R);
   const size_t lds = sizeof(int) * (size_t)E_local;
   hipLaunchKernelGGL(perm_count_kernel, dim3(n_chunks), dim3(256), lds, stream, idx, R, offset,
-                     E_local, counts);
+                     E_local, chunk, counts);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, R, E_local,
                      n_chunks, counts, offs, sorted_route, tile_prefix);
   hipLaunchKernelGGL(perm_rank_kernel, dim3(n_chunks), dim3(64), lds, stream, idx, R, offset,
-                     E_local, counts, sorted_route, route_row);
+                     E_local, chunk, counts, sorted_route, route_row);
   return hipGetLastError();
 }
 

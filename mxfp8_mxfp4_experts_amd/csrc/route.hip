@@ -4,13 +4,14 @@
 // scores, the correction bias only takes part in choosing experts, the weights
 // gather the bias-free scores and are normalised; page 5: routed scaling.
 //
-// One 64-lane wavefront per token; the slots come out ordered by key
-// descending, ties going to the lower expert index.
-//  * E <= 1024: lane l holds the keys of experts l, l + 64, ... in registers
-//    (as order-preserving unsigned integers).  Each of the K rounds takes the
-//    lane's best remaining key, the wavefront maximum of those (DPP row
-//    shifts and broadcasts), then the smallest expert index among the lanes
-//    holding that maximum; the owning lane retires the winner.
+// The slots come out ordered by key descending, ties going to the lower
+// expert index.
+//  * E <= 1024: one workgroup per token computes the keys (as
+//    order-preserving unsigned integers) into LDS; then lane l of the first
+//    wavefront holds the keys of experts l, l + 64, ... in registers.  Each of
+//    the K rounds takes the lane's best remaining key, the wavefront maximum
+//    of those (DPP row shifts and broadcasts), then the smallest expert index
+//    among the lanes holding that maximum; the owning lane retires the winner.
 //  * larger E: the keys sit in LDS and each round takes a wavefront arg-max
 //    over a 64-bit key (ordered float key, then inverted expert index)
 //    restricted to keys below the previous winner.
@@ -61,23 +62,27 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 
 constexpr int kRegExpertsPerLane = 16;   // register path: E <= 1024
 
-__global__ __launch_bounds__(64 * kRouteWaves) void route_reg_kernel(
+// One workgroup per token: its four wavefronts compute the keys (the double
+// precision sigmoid is the costly part) into LDS, then the first wavefront
+// selects.
+__global__ __launch_bounds__(256) void route_reg_kernel(
     const float* __restrict__ logits, int64_t ld, const float* __restrict__ bias, int T, int E,
     int K, float scaling, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kRouteWaves + wave;
-  if (t >= T) return;                                // uniform per wavefront
+  __shared__ uint32_t keys_s[64 * kRegExpertsPerLane];
+  const int t = blockIdx.x;
   const float* row = logits + (size_t)t * ld;
+  for (int e = threadIdx.x; e < E; e += 256)
+    keys_s[e] = ordered_key(sigmoid_score(row[e]) + (bias ? bias[e] : 0.0f));
+  __syncthreads();
+  if (threadIdx.x >= 64) return;                     // whole wavefronts leave
+  const int lane = threadIdx.x;
   uint32_t key[kRegExpertsPerLane];
   uint32_t avail = 0;                                // bit j: expert lane + 64 j not yet taken
 #pragma unroll
   for (int j = 0; j < kRegExpertsPerLane; ++j) {
     const int e = lane + 64 * j;
-    key[j] = 0;
-    if (e < E) {
-      key[j] = ordered_key(sigmoid_score(row[e]) + (bias ? bias[e] : 0.0f));
-      avail |= 1u << j;
-    }
+    key[j] = e < E ? keys_s[e] : 0u;
+    avail |= (e < E ? 1u : 0u) << j;
   }
   int my_id = 0;
   for (int k = 0; k < K; ++k) {
@@ -149,8 +154,8 @@ hipError_t launch_route(const float* logits, int64_t ld, const float* bias, int 
                         float scaling, int32_t* idx, float* w, hipStream_t stream) {
   int blocks = (T + kRouteWaves - 1) / kRouteWaves;
   if (E <= 64 * kRegExpertsPerLane) {
-    hipLaunchKernelGGL(route_reg_kernel, dim3(blocks), dim3(64 * kRouteWaves), 0, stream, logits,
-                       ld, bias, T, E, K, scaling, idx, w);
+    hipLaunchKernelGGL(route_reg_kernel, dim3(T), dim3(256), 0, stream, logits, ld, bias, T, E, K,
+                       scaling, idx, w);
     return hipGetLastError();
   }
   size_t lds = sizeof(float) * (size_t)E * kRouteWaves;

@@ -171,7 +171,8 @@ def test_prepack_matches_documented_layout(which):
 
 @pytest.mark.parametrize("T,K,E,E_local,offset", [
     (200, 8, 600, 300, 100),      # one workgroup (at most 2048 routes)
-    (5000, 8, 600, 300, 100),     # chunked grouping: 20 chunks, ragged last one
+    (700, 8, 600, 300, 100),      # 256-route chunks: 22, ragged last one
+    (5000, 8, 600, 300, 100),     # 2048-route chunks: 20, ragged last one
     (4096, 16, 64, 64, 0),        # exactly 32 chunks, every expert hot
 ])
 def test_grouping_matches_oracle(T, K, E, E_local, offset):
