@@ -1,0 +1,77 @@
+// a8: top-k weighted combine of the FC2 rows (page 1, "Serving 调用链": the
+// finalize step after GEMM2; "对称性约束": the non-fused, deterministic
+// finalize).  out[t] = bf16 of the sum over kept slots k, in slot order, of
+// w[t,k] * y[route_row[t,k]], accumulated in float32; masked and dropped
+// slots contribute nothing, and a token with no kept slot gets zeros.
+#include "common.h"
+#include "fc_common.h"
+#include "launch.h"
+
+namespace mi355moe {
+
+namespace {
+
+// out[t] = bf16( sum over kept k, in k order, of w[t,k] * y[route_row[t,k]] ).
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int H,
+                                                      const int32_t* __restrict__ route_row,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int K, uint16_t* __restrict__ out,
+                                                      int64_t ld_out) {
+  const int per_row = H / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * per_row) return;
+  const int t = (int)(gid / per_row), c = (int)(gid % per_row);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // Slots in groups of 16: all route rows and weights of the group first,
+  // then all row loads (independent, in flight together), then the sums in
+  // slot order.
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    int rr[16];
+    float wk[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int k = k0 + j;
+      rr[j] = k < K ? route_row[(size_t)t * K + k] : -1;
+      wk[j] = k < K ? topk_w[(size_t)t * K + k] : 0.0f;
+    }
+    v4f a[16], b[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      a[j] = v4f{0.f, 0.f, 0.f, 0.f};
+      b[j] = a[j];
+      if (rr[j] >= 0) {
+        const v4f* src = reinterpret_cast<const v4f*>(y + (size_t)rr[j] * H + (size_t)c * 8);
+        a[j] = src[0];
+        b[j] = src[1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (rr[j] < 0) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = fmaf(wk[j], a[j][i], acc[i]);
+        acc[4 + i] = fmaf(wk[j], b[j][i], acc[4 + i]);
+      }
+    }
+  }
+  uint4 o;
+  o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+  o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+  o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+  o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * ld_out + (size_t)c * 8) = o;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,
+                          int T, int K, uint16_t* out, int64_t ld_out, hipStream_t stream) {
+  const int64_t threads = (int64_t)T * (H / 8);
+  const int blocks = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, y, H, route_row, topk_w,
+                     T, K, out, ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace mi355moe
