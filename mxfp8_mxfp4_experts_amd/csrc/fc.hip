@@ -1,5 +1,6 @@
-// a4..a8: grouped FC1 (+ SiTU + requantisation) and FC2 (+ combine) on the
-// gfx950 block-scaled MFMA (V_MFMA_SCALE_F32_16X16X128_F8F6F4).
+// a4..a7: grouped FC1 (+ SiTU + requantisation) and FC2 (writing the per-route
+// rows the combine sums) on the gfx950 block-scaled MFMA
+// (V_MFMA_SCALE_F32_16X16X128_F8F6F4), for experts holding few grouped rows.
 //
 // Page 1, "Serving call chain": grouped GEMM1 -> gated activation -> GEMM2 ->
 // finalize; "Real checkpoint contract": w13 = [gate; up] halves, SiTU(4, 25);
