@@ -77,7 +77,7 @@ const char* moe_strerror(int status) {
 
 size_t moe_workspace_size(int T, int top_k, int E_local, int H, int I) {
   if (!valid_hi(H, I) || !valid_window(top_k, E_local) || !valid_rows(T, top_k, H, I)) return 0;
-  return ws_layout(T, top_k, E_local, H).total;
+  return ws_layout(T, top_k, E_local, H, I).total;
 }
 
 moe_status_t moe_route(const float* logits, int64_t ld_logits, const float* bias, int T, int E,
@@ -124,10 +124,10 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int top_k, int expert_o
       (T > 0 && (!aligned(topk_idx, 4) || !aligned(sorted_route, 4) || !aligned(route_row, 4))))
     return MOE_ERR_ALIGN;
   // The schedule part of the workspace does not depend on H.
-  if (ws_bytes < ws_layout(T, top_k, E_local, 0).y) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_layout(T, top_k, E_local, 0, 0).y) return MOE_ERR_WORKSPACE;
   moe_status_t s = check_device();
   if (s != MOE_OK) return s;
-  WsLayout l = ws_layout(T, top_k, E_local, 0);
+  WsLayout l = ws_layout(T, top_k, E_local, 0, 0);
   int32_t* prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.tile_prefix);
   int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.perm_counts);
   return finish(launch_permute(topk_idx, T * top_k, expert_offset, E_local, expert_offsets,
@@ -151,16 +151,18 @@ static moe_status_t fc1_impl(const uint8_t* xq, const uint8_t* xs, int T, int H,
   if (T > 0 && (!aligned(xq, 16) || !aligned(xs, 16) || !aligned(sorted_route, 4) ||
                 !aligned(hq, 16) || !aligned(hs, 4)))
     return MOE_ERR_ALIGN;
-  WsLayout l = ws_layout(T, top_k, E_local, H);
+  WsLayout l = ws_layout(T, top_k, E_local, H, I);
   if (ws_bytes < l.y) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
   int n_cu = 0;
   moe_status_t s = check_device(&n_cu);
   if (s != MOE_OK) return s;
-  const int32_t* prefix =
-      reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + l.tile_prefix);
+  char* ws = static_cast<char*>(workspace);
+  const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + l.tile_prefix);
+  uint32_t* act_st = reinterpret_cast<uint32_t*>(ws + l.act_st);
   return finish(launch_fc1(xq, xs, T, H, I, top_k, E_local, expert_offsets, sorted_route, w13,
-                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, n_cu, tiled, stream));
+                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, act_st, n_cu, tiled,
+                           stream));
 }
 
 moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
@@ -198,7 +200,7 @@ static moe_status_t fc2_impl(const uint8_t* hq, const uint8_t* hs, int T, int H,
   if (T > 0 && (!aligned(hq, 16) || !aligned(hs, 16) || !aligned(route_row, 4) ||
                 !aligned(topk_w, 4) || !aligned(out, 16) || ld_out % 8 != 0))
     return MOE_ERR_ALIGN;
-  WsLayout l = ws_layout(T, top_k, E_local, H);
+  WsLayout l = ws_layout(T, top_k, E_local, H, I);
   if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
   int n_cu = 0;
@@ -207,8 +209,9 @@ static moe_status_t fc2_impl(const uint8_t* hq, const uint8_t* hs, int T, int H,
   char* ws = static_cast<char*>(workspace);
   const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + l.tile_prefix);
   float* y = reinterpret_cast<float*>(ws + l.y);
+  uint32_t* act_st = reinterpret_cast<uint32_t*>(ws + l.act_st);
   hipError_t e = launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, prefix,
-                            n_cu, tiled, stream);
+                            act_st, n_cu, tiled, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return finish(launch_combine(y, H, route_row, topk_w, T, top_k, out, ld_out, stream));
 }

@@ -33,19 +33,23 @@ inline int perm_chunks(int64_t R) {
 struct WsLayout {
   size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1]
   size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
+  size_t act_st;        // uint32 [max(H, I) / 128][T * top_k]: an FC input's scale dwords,
+                        // stage-major in grouped-row order (prefill-shaped FC kernels)
   size_t y;             // float [T * top_k][H]  (FC2 rows before the combine)
   size_t total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(int T, int top_k, int E_local, int H) {
+inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I) {
   WsLayout l;
   size_t off = 0;
   l.tile_prefix = off;
   off = align256(off + sizeof(int32_t) * kNumTileSizes * (size_t)(E_local + 1));
   l.perm_counts = off;
   off = align256(off + sizeof(int32_t) * (size_t)perm_chunks((int64_t)T * top_k) * E_local);
+  l.act_st = off;
+  off = align256(off + (size_t)T * top_k * (size_t)((H > I ? H : I) / 32));
   l.y = off;
   off = align256(off + sizeof(float) * (size_t)T * top_k * H);
   l.total = off;

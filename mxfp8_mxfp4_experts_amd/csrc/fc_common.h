@@ -22,6 +22,8 @@ struct FcParams {
   const uint8_t* act;        // FC1: xq [T, K]; FC2: hq [R, K]
   const uint8_t* act_s;      // [.., K/32]
   int64_t act_rows;          // rows of act: FC1 T, FC2 R
+  int64_t n_routes;          // grouped rows R = T * top_k
+  uint32_t* act_st;          // workspace: [K/128][R] scale dwords of the grouped rows
   const int32_t* gather;     // FC1: sorted_route (grouped row -> route); FC2: unused
   int top_k;
   const uint8_t* w;          // [E_local, N, K/2]

@@ -4,32 +4,44 @@
 // GEMM1 -> gated activation -> GEMM2; "真实 checkpoint 契约": [gate; up] halves,
 // SiTU(4, 25); page 5: w13 / w2 and scale layouts), organised for experts
 // that hold tens to hundreds of grouped rows:
-//   * a workgroup of 4 wavefronts (one per SIMD, each with the whole register
-//     file) computes up to 256 grouped rows of one expert against 256 weight
-//     rows.  Wavefront w owns one 64-row unit (FC1: gate rows [c, c+32) with
-//     up rows [I+c, I+c+32), so SiTU pairs stay in one wavefront; FC2: 64
-//     output columns) and all 256 token rows: 4 row blocks x 16 token tiles
-//     of 16x16 accumulators, 256 AGPRs;
+//   * a workgroup of 8 wavefronts (two per SIMD, so one wavefront's waits are
+//     covered by the other's MFMAs) computes up to 256 grouped rows of one
+//     expert against 256 weight rows.  Wavefront w owns weight half w & 1
+//     (two 64-row units: FC1 gate rows [c, c+32) with up rows [I+c, I+c+32),
+//     so SiTU pairs stay in one wavefront; FC2 64 output columns each) and
+//     token quarter w >> 1 (the 16-row tiles q, q+4, q+8, q+12, so a partly
+//     filled tile still spreads over all four SIMDs): 4 tiles x 8 row blocks
+//     of 16x16 accumulators, 128 AGPRs;
+//   * both operands go through a ring of 3 LDS stages of 50 KB (256 token
+//     rows x 128 bytes, 256 token scale dwords, 256 weight rows x 64 bytes,
+//     256 weight scale dwords), filled by direct buffer -> LDS loads two
+//     stages ahead: every wavefront issues 7 per stage (4 KB of token rows,
+//     2 KB of weights, and the token or the weight scale dwords), so one
+//     fixed "s_waitcnt vmcnt(7)" per stage leaves exactly the next stage in
+//     flight; past the last stage the final stage is reloaded to keep that
+//     count.  The loads sit in the odd MFMA slots of the first two tiles
+//     (early in the stage: the longest lead before their wait);
+//   * the token scale dwords are first restaged (stage_scales_kernel) into a
+//     stage-major array in grouped-row order, so a tile's scales for one stage
+//     are one contiguous 1 KB run instead of one cache line per row: the
+//     per-CU load path is bounded by outstanding cache-line requests, not by
+//     bytes;
+//   * token 16-byte chunks are XOR-swizzled by row bits 0..2 and weight chunks
+//     sit in the tiled layout's order, so the eight lanes served together hit
+//     eight bank groups;
 //   * an expert with at most 256 rows is one tile, so its weights are read
 //     once in total; its token rows are re-read by every column group, which
-//     the XCD-contiguous schedule keeps in that XCD's L2.  The tiles of a hot
-//     expert run side by side on one column group, sharing its weights;
-//   * weights go from memory straight to registers: one coalesced 16-byte
-//     load per lane per 16-row block and stage (in the tiled layout each
-//     block's MFMA operand is one contiguous 1 KB piece in lane order), three
-//     stages ahead in four rotating register sets;
-//   * token rows go through a ring of 4 LDS stages (256 rows x 128 bytes +
-//     one scale dword per row), filled by direct buffer -> LDS loads three
-//     stages ahead; 16-byte chunks are XOR-swizzled by row bits 0..2 so the
-//     eight lanes served together hit eight bank groups;
-//   * token tiles are taken in pairs; pairs past the expert's last row are
-//     skipped (at most one empty 16-row tile is computed).  Each of a pair's
-//     8 MFMAs is followed by one LDS read of the next pair and, on odd ones,
-//     one global load of stage s + 3, so reads and loads issue under the
-//     MFMAs rather than in bursts.  Every wavefront issues the same 17 loads
-//     per stage (9 direct-to-LDS, then 8 to registers), so one fixed
-//     "s_waitcnt vmcnt" per stage leaves exactly the later stages in flight;
-//     past the last stage the final stage is reloaded to keep that count;
+//     the XCD-contiguous schedule keeps in that XCD's L2;
+//   * per stage a wavefront reads its 8 weight operands once, then per valid
+//     token tile 8 MFMAs, each followed by a read of the next tile's operands
+//     or one of the stage's global loads.  The stage loop is instantiated per
+//     count of valid tiles (0..4), so no accumulator is updated under a
+//     condition (which the register allocator handles by copying);
+//   * the expert tile prefix and row offsets are copied to LDS once per
+//     workgroup (the item lookup is a binary search per item).  The stage
+//     ring and this table are one LDS object: with several, the compiler
+//     cannot tell the direct-to-LDS loads from the operand reads and waits
+//     for every load before each read;
 //   * buffer resources keep every per-lane address a 32-bit offset.
 #include "common.h"
 #include "fc_common.h"
@@ -42,29 +54,26 @@ namespace mi355moe {
 
 namespace {
 
-constexpr int kBM = 256;                    // token rows per tile
-constexpr int kBN = 256;                    // weight rows per tile (4 units)
-constexpr int kKS = 128;                    // K per stage
-constexpr int kABytes = kBM * kKS;          // 32768: E4M3 token slice
-constexpr int kASBytes = kBM * 4;           // 1024: one scale dword per token row
-constexpr int kStage = kABytes + kASBytes;  // 33792
-constexpr int kNumBuf = 4;                  // LDS ring depth
-constexpr int kThreads = 256;
-constexpr int kTilePrefixIndex = 4;         // tile height 16 << 4 = 256
-constexpr int kNt = 2;                      // nontemporal policy for weight loads
+constexpr int kBM = 256;                     // token rows per tile
+constexpr int kBN = 256;                     // weight rows per tile (4 units)
+constexpr int kKS = 128;                     // K per stage
+constexpr int kThreads = 512;                // 8 wavefronts
+constexpr int kTokScaleOff = kBM * kKS;      // 32768: token scale dwords
+constexpr int kWOff = kTokScaleOff + kBM * 4;        // 33792: weight operands
+constexpr int kWScaleOff = kWOff + kBN * kKS / 2;    // 50176: weight scale dwords
+constexpr int kStage = kWScaleOff + kBN * 4;         // 51200
+constexpr int kNumBuf = 3;                   // LDS ring depth
+constexpr int kTilePrefixIndex = 4;          // tile height 16 << 4 = 256
+constexpr int kMaxLdsExperts = 1024;            // local experts whose metadata LDS holds
 static_assert(kKS == kTileK && 2 * kBN == kTileRows, "tile shape");
 static_assert((16 << kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSizes, "tile prefix");
+constexpr int kLdsBytes = kNumBuf * kStage + 8 * (kMaxLdsExperts + 1);
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
-// Loads issued per wavefront and stage: 9 direct-to-LDS (token rows and
-// their scales), then 8 to registers (weight blocks and scale bytes).  When
-// stage s is waited for (token rows and weights), the loads issued after it
-// are the next two stages': 2 * 17 = 34.
-constexpr int kActLoads = 9, kWLoads = 8;
-constexpr int kLoadsPerStage = kActLoads + kWLoads;
-constexpr int kWaitCount = 2 * kLoadsPerStage;   // 34
-static_assert(kWaitCount < 64, "vmcnt range");
-// First load of each tile pair's share (pair 7 issues none).
-constexpr int kLoadStart[9] = {0, 3, 6, 9, 11, 13, 15, 17, 17};
+// Loads issued per wavefront and stage: 4 token pieces, 2 weight pieces and
+// 1 scale piece, all direct to LDS.  When stage s + 1 is waited for, only
+// stage s + 2's 7 remain in flight.
+constexpr int kLoadsPerStage = 7;
 
 // Raw buffer resource: base and byte size in SGPRs.  Sizes stay below 2^31,
 // so kOutOfRange (plus any stage offset) is always past the end.
@@ -83,14 +92,18 @@ __device__ __forceinline__ void static_for(F& f) {
   }
 }
 
+// Largest expert e with prefix[e] <= tile, from the LDS copy.
+__device__ __forceinline__ int find_expert_lds(const int* prefix, int E_local, int tile) {
+  int lo = 0, hi = E_local;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= tile) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 typedef __attribute__((address_space(3))) uint8_t lds_t;
 typedef __attribute__((address_space(3))) v4i lds_v4i;
-
-// Weight operands of one stage for one wavefront: 4 row blocks.
-struct WStage {
-  v4i w[4];
-  int s[4];
-};
 
 // Token operands of one 16-row tile: K [16g, +16) and [64 + 16g, +16) for
 // lane group g, and the row's scale byte for MX block g.
@@ -99,280 +112,293 @@ struct AOp {
   int sc;
 };
 
+// Scale dwords of the grouped rows, stage-major: out[s][r] = the four E8M0
+// bytes of MX blocks 4s .. 4s+3 of grouped row r's source row (FC1: token
+// gather[r] / top_k of act_s; FC2: row r).  The prefill kernels then load a
+// tile's scales for a stage as one contiguous run instead of one cache line
+// per row.  Only the kept rows [0, offs[E_local]) are written.
+__global__ __launch_bounds__(256) void stage_scales_kernel(const uint8_t* __restrict__ act_s,
+                                                           int k32, const int32_t* __restrict__ gather,
+                                                           int top_k, const int32_t* __restrict__ offs,
+                                                           int E_local, int R, int n_stages,
+                                                           uint32_t* __restrict__ out) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= offs[E_local]) return;
+  const int src = gather ? gather[r] / top_k : r;
+  const uint32_t* row = reinterpret_cast<const uint32_t*>(act_s + (size_t)src * k32);
+  for (int s = 0; s < n_stages; ++s) out[(size_t)s * R + r] = row[s];
+}
+
 template <bool FC1, bool TILED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fc_prefill_kernel(FcParams p, int n_cg) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kNumBuf * kStage];
+  // One LDS object: the stage ring, then the expert tile prefix and row
+  // offsets (read once per workgroup).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+  int* const prefix_s = reinterpret_cast<int*>(lds + kNumBuf * kStage);
+  int* const offs_s = prefix_s + kMaxLdsExperts + 1;
   lds_t* const lds_base = (lds_t*)lds;   // LDS address space: immediate offsets fold
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
+  const int hw = wave & 1, qt = wave >> 1;                     // weight half, token quarter
   const int g = lane >> 4, li = lane & 15;
   const int K = p.K;
   const int n_stages = K / kKS;
-  const int* prefix = p.tile_prefix;
-  const int n_items = prefix[p.E_local] * n_cg;
+  for (int i = tid; i <= p.E_local; i += kThreads) {
+    prefix_s[i] = p.tile_prefix[i];
+    offs_s[i] = p.expert_offsets[i];
+  }
+  __syncthreads();
+  const int n_items = prefix_s[p.E_local] * n_cg;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
   const int item_lo = (int)((int64_t)n_items * xcd / 8);
   const int item_hi = (int)((int64_t)n_items * (xcd + 1) / 8);
   const __amdgpu_buffer_rsrc_t act_r = rsrc(p.act, (uint32_t)(p.act_rows * K));
-  const __amdgpu_buffer_rsrc_t acts_r = rsrc(p.act_s, (uint32_t)(p.act_rows * (K / 32)));
 
-  // Items run expert by expert; inside an expert column group by column
-  // group, and inside a column group tile by tile: neighbouring items share
-  // either the weights (tiles of one hot expert) or the token rows (column
-  // groups of one tile).  Expert e owns items [n_cg prefix[e], n_cg prefix[e+1]).
+  // LDS read offsets (lane parts; the tile's part goes into the immediate):
+  // token tile tt = qt + 4 j at 2048 tt, its scale bytes at 64 tt; weight
+  // operand (unit 2 hw + k, block i) is 1 KB piece 4 (2 hw + k) + i, lane
+  // (li, g) at position 4 li + (g ^ ((li >> 1) & 3)); its scale byte is byte
+  // g of row 64 (2 hw + k) + 16 i + li's dword.
+  const int a_lo = 2048 * qt + li * kKS + 16 * (g ^ (li & 7));
+  const int a_hi = 2048 * qt + li * kKS + 16 * ((4 + g) ^ (li & 7));
+  const int a_sc = kTokScaleOff + 64 * qt + 4 * li + g;
+  const int b_op = kWOff + 8192 * hw + 16 * (4 * li + (g ^ ((li >> 1) & 3)));
+  const int b_sc = kWScaleOff + 512 * hw + 4 * li + g;
+
   for (int item = item_lo + slot; item < item_hi; item += per_xcd) {
-    const int e = __builtin_amdgcn_readfirstlane(find_expert(prefix, p.E_local, item / n_cg));
-    const int nt = prefix[e + 1] - prefix[e];
-    const int local = item - prefix[e] * n_cg;
+    const int e = __builtin_amdgcn_readfirstlane(find_expert_lds(prefix_s, p.E_local, item / n_cg));
+    const int pe = __builtin_amdgcn_readfirstlane(prefix_s[e]);
+    const int nt = __builtin_amdgcn_readfirstlane(prefix_s[e + 1]) - pe;
+    const int local = item - pe * n_cg;
     const int cg = local / nt, t_in_e = local - cg * nt;
-    const int row_begin = p.expert_offsets[e] + t_in_e * kBM;
-    const int n_valid = min(p.expert_offsets[e + 1] - row_begin, kBM);
-    const int npairs = (n_valid + 31) >> 5;                     // token tile pairs in use
-    const int unit = 4 * cg + wave;                             // global 64-row unit
+    const int row_begin = __builtin_amdgcn_readfirstlane(offs_s[e]) + t_in_e * kBM;
+    const int n_valid = min(__builtin_amdgcn_readfirstlane(offs_s[e + 1]) - row_begin, kBM);
+    const int ntiles = (n_valid + 15) >> 4;                      // 16-row tiles in use
+    const int nj = ntiles > qt ? (ntiles - qt + 3) >> 2 : 0;     // this wavefront's tiles
+    const int rows_used = 16 * ntiles;
 
-    // Weights of row block i of this wavefront's unit (rows 16 i + li):
-    // lane offset + SGPR offset per block and stage.  Each lane reads only
-    // its scale byte (MX block 4 s + g of its row).
-    __amdgpu_buffer_rsrc_t w_r, ws_r;
-    uint32_t w_voff, ws_voff;
-    int w_soff[4], ws_soff[4], w_step, ws_step;
+    // Weight pieces: wavefront w copies 1 KB pieces c = 2 w, 2 w + 1 (unit
+    // c / 4, row block c % 4).  Scale dwords: wavefronts 0..3 copy token
+    // rows 64 w + l, wavefronts 4..7 weight rows 64 (w - 4) + l.
+    __amdgpu_buffer_rsrc_t w_r, s_r;
+    uint32_t w_voff[2], s_voff;
+    int w_step, s_step;
     if (TILED) {
-      // 512-row group cg / 2 holds units 8 (cg / 2) .. + 7; this unit is its
-      // (4 (cg & 1) + wave)-th.
-      const int u8 = 4 * (cg & 1) + wave;
       const size_t blk0 = tiled_block(e, cg >> 1, 0, n_cg >> 1, n_stages);
-      w_r = rsrc(p.w + blk0 * kTileBytes, (uint32_t)n_stages * kTileBytes);
-      ws_r = rsrc(p.w_s + blk0 * kTileScaleBytes, (uint32_t)n_stages * kTileScaleBytes);
-      w_voff = 4096 * u8 + 16 * (4 * li + (g ^ ((li >> 1) & 3)));
-      ws_voff = 4 * (64 * u8 + li) + g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w_soff[i] = 1024 * i;
-        ws_soff[i] = 64 * i;
-      }
+      w_r = rsrc(p.w + blk0 * kTileBytes + 16384 * (cg & 1), (uint32_t)n_stages * kTileBytes);
       w_step = kTileBytes;
-      ws_step = kTileScaleBytes;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) w_voff[x] = 1024 * (2 * wave + x) + 16 * lane;
     } else {
       const size_t e_rows = (size_t)e * p.N;
       w_r = rsrc(p.w + e_rows * (K / 2), (uint32_t)p.N * (K / 2));
-      ws_r = rsrc(p.w_s + e_rows * (K / 32), (uint32_t)p.N * (K / 32));
-      w_voff = li * (K / 2) + 16 * g;
-      ws_voff = li * (K / 32) + g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // FC1: blocks 0, 1 are gate rows 32 unit + 16 i, blocks 2, 3 the
-        // matching up rows I + 32 unit + 16 (i - 2); FC2: rows 64 unit + 16 i.
-        const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * unit + 16 * (i & 1) : 64 * unit + 16 * i;
-        w_soff[i] = rb * (K / 2);
-        ws_soff[i] = rb * (K / 32);
-      }
       w_step = 64;
-      ws_step = 4;
-    }
-    // Token rows: wavefront w fills rows 64 w + 8 i + l / 8 (i < 8); physical
-    // chunk l % 8 of a row takes logical chunk (l % 8) ^ (row & 7).  Scale
-    // dwords: rows 64 w + l.  Rows past the expert's last, inside the last
-    // tile pair, repeat that row; rows of skipped pairs get an offset past
-    // the buffer's end, which the buffer unit answers with zeros without
-    // touching memory (so every wavefront still issues the same loads).
-    uint32_t a_voff[8];
-    const int ac = (lane & 7) ^ ((lane >> 3) & 7);
-    const int rows_used = 32 * npairs;
+      // Position l of a piece holds row l / 4 of the block and logical
+      // 16-byte chunk (l & 3) ^ ((l >> 3) & 3) (the tiled layout's order).
+      const int r = lane >> 2, ch = (lane & 3) ^ ((lane >> 3) & 3);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tok = 64 * wave + 8 * i + (lane >> 3);
-      const int row = row_begin + min(tok, n_valid - 1);
-      const int src = FC1 ? p.gather[row] / p.top_k : row;
-      a_voff[i] = tok < rows_used ? (uint32_t)src * K + 16 * ac : kOutOfRange;
+      for (int x = 0; x < 2; ++x) {
+        const int c = 2 * wave + x, u = 4 * cg + (c >> 2), i = c & 3;
+        const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * u + 16 * (i & 1) : 64 * u + 16 * i;
+        w_voff[x] = (uint32_t)(rb + r) * (K / 2) + 16 * ch;
+      }
     }
-    uint32_t as_voff;
-    {
-      const int tok = 64 * wave + lane;
+    // LDS place of this wavefront's scale dwords.
+    const int s_lds = wave < 4 ? kTokScaleOff + 256 * wave : kWScaleOff + 256 * (wave - 4);
+    // Source rows of the token pieces (four per lane): all gather reads are
+    // issued before any is used, so their latencies overlap.  Rows past the
+    // expert's last repeat that row.
+    int src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 32 * wave + 8 * i + (lane >> 3);
       const int row = row_begin + min(tok, n_valid - 1);
-      const int src = FC1 ? p.gather[row] / p.top_k : row;
-      as_voff = tok < rows_used ? (uint32_t)src * (K / 32) : kOutOfRange;
+      src[i] = FC1 ? p.gather[row] : row;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      asm volatile("" : "+v"(src[i]));
+      if (FC1) src[i] /= p.top_k;
+    }
+    if (wave < 4) {
+      // The token scale dwords of stage s are the contiguous run
+      // act_st[s][row_begin ..]: one coalesced piece per wavefront.
+      s_r = rsrc(p.act_st, (uint32_t)(n_stages * p.n_routes * 4));
+      s_step = (int)(4 * p.n_routes);
+      const int tok = 64 * wave + lane;
+      s_voff = tok < rows_used ? 4u * (uint32_t)(row_begin + tok) : kOutOfRange;
+    } else if (TILED) {
+      const size_t blk0 = tiled_block(e, cg >> 1, 0, n_cg >> 1, n_stages);
+      s_r = rsrc(p.w_s + blk0 * kTileScaleBytes + 1024 * (cg & 1),
+                 (uint32_t)n_stages * kTileScaleBytes);
+      s_step = kTileScaleBytes;
+      s_voff = 4 * (64 * (wave - 4) + lane);
+    } else {
+      const size_t e_rows = (size_t)e * p.N;
+      s_r = rsrc(p.w_s + e_rows * (K / 32), (uint32_t)p.N * (K / 32));
+      s_step = 4;
+      const int r = 64 * (wave - 4) + lane, u = 4 * cg + (r >> 6), i = (r >> 4) & 3;
+      const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * u + 16 * (i & 1) : 64 * u + 16 * i;
+      s_voff = (uint32_t)(rb + (r & 15)) * (K / 32);
+    }
+    // Token rows: wavefront w fills rows 32 w + 8 i + l / 8 (i < 4); physical
+    // chunk l % 8 of a row takes logical chunk (l % 8) ^ (row & 7).  Rows of
+    // unused tiles get an offset past the buffer's end, which the buffer unit
+    // answers with zeros without touching memory (so every wavefront still
+    // issues the same loads).
+    uint32_t a_voff[4];
+    const int ac = (lane & 7) ^ ((lane >> 3) & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = 32 * wave + 8 * i + (lane >> 3);
+      a_voff[i] = tok < rows_used ? (uint32_t)src[i] * K + 16 * ac : kOutOfRange;
     }
 
-    // Load q (0..16) of stage s_load: q < 8 a 1 KB piece of token rows, q = 8
-    // the token scale dwords (direct to LDS, stage buffer s_load % 4); q < 13
-    // a weight block, q < 17 a weight scale byte (to register set ws).
-    auto issue_load = [&](int q, WStage& ws, int s_load) __attribute__((always_inline)) {
-      // Recomputed per load (cheap scalar work) rather than kept in scalar
-      // registers across the loop.
+    // Load q (0..6) of stage s_load into stage buffer s_load % 3: q < 4 a 1 KB
+    // piece of token rows, q = 4, 5 a weight piece, q = 6 the scale dwords.
+    auto issue_load = [&](int q, int s_load) __attribute__((always_inline)) {
       asm volatile("" : "+s"(s_load));
       const int sc = min(s_load, n_stages - 1);
       uint8_t* base = lds + (s_load % kNumBuf) * kStage;
-      if (q < 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + wave * 8192 + q * 1024, 16,
+      if (q < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + 4096 * wave + 1024 * q, 16,
                                                  a_voff[q], kKS * sc, 0, 0);
-      else if (q == 8)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(acts_r, base + kABytes + wave * 256, 4, as_voff,
-                                                 4 * sc, 0, 0);
-      else if (q < 13)
-        // Weight loads are issued in assembly so that the compiler does not
-        // place its own (conservative) waits for them; the stage-end wait
-        // covers them and the registers are re-pinned after it.
-        asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen nt"
-                     : "=v"(ws.w[q - 9])
-                     : "v"(w_voff), "s"(w_r), "s"(w_soff[q - 9] + sc * w_step));
+      else if (q < 6)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_r, base + kWOff + 1024 * (2 * wave + q - 4), 16,
+                                                 w_voff[q - 4], w_step * sc, 0, 0);
       else
-        asm volatile("buffer_load_ubyte %0, %1, %2, %3 offen"
-                     : "=v"(ws.s[q - 13])
-                     : "v"(ws_voff), "s"(ws_r), "s"(ws_soff[q - 13] + sc * ws_step));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_r, base + s_lds, 4, s_voff, s_step * sc, 0, 0);
     };
 
-    v4f acc[16][4];  // [token tile][row block]
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[tt][i] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    // Token operands of tile tt from stage buffer A: lane parts of the
-    // addresses here, the tile's part (2048 tt, or 64 tt for the scale byte)
-    // goes into the LDS instructions' immediate offset.
-    const int a_lo = li * kKS + 16 * (g ^ (li & 7));
-    const int a_hi = li * kKS + 16 * ((4 + g) ^ (li & 7));
-    const int a_sc = kABytes + 4 * li + g;
-    auto read_a = [&](AOp& o, const lds_t* A, int tt) __attribute__((always_inline)) {
-      o.lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 2048 * tt);
-      o.hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 2048 * tt);
-      o.sc = A[a_sc + 64 * tt];
-    };
     // Stage buffer of stage s.  The offset is made opaque so that the compiler
-    // cannot prove later pairs' reads in bounds and hoist them above the pair
-    // conditions (which would hold every pair's operands at once).
+    // cannot prove later tiles' reads in bounds and hoist them.
     auto stage_buf = [&](int s) __attribute__((always_inline)) {
       int off = (s % kNumBuf) * kStage;
       asm volatile("" : "+s"(off));
       return static_cast<const lds_t*>(lds_base) + off;
     };
 
-    AOp buf[2][2];   // [pair parity][tile of the pair]
-    // One stage.  Pair pp: 8 MFMAs; after MFMA j < 6 one LDS read of pair
-    // pp + 1, after MFMAs 1, 3, 5 the pair's share of the 17 global loads of
-    // stage s + 3 (token rows into the buffer stage s - 1 used, weights into
-    // register set nw), so neither the reads nor the loads stall the MFMAs.
-    // Skipped pairs still issue their loads: every stage issues the same 17,
-    // token rows (0..8) before weights (9..16).  Pair 0's operands were read
-    // before the call.
-    auto compute = [&](const WStage& ws, WStage& nw, int s) __attribute__((always_inline)) {
-      const lds_t* A = stage_buf(s);
-      auto pair_fn = [&](auto ppi) __attribute__((always_inline)) {
-        constexpr int pp = decltype(ppi)::value;
-        constexpr int q0 = kLoadStart[pp], q1 = kLoadStart[pp + 1];
-        if (pp < npairs) {
-          AOp(&cur)[2] = buf[pp & 1];
-          AOp(&nxt)[2] = buf[(pp + 1) & 1];
+    // The stage loop for a wavefront holding NJ valid token tiles (a
+    // compile-time count, so no accumulator is conditionally updated).
+    auto run = [&](auto nji) __attribute__((always_inline)) {
+      constexpr int NJ = decltype(nji)::value;
+      v4f acc[NJ > 0 ? NJ : 1][2][4];  // [token tile j][unit k][row block i]
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int h = j >> 2, i = j & 3;
-            acc[2 * pp + h][i] =
-                mfma_w4a8<0>(ws.w[i], cur[h].lo, cur[h].hi, acc[2 * pp + h][i], ws.s[i], cur[h].sc);
-            if constexpr (pp + 1 < 8) {
-              // Both scale bytes, then tile 0's operand, then tile 1's (the
-              // next pair's first MFMAs wait only for what they use).
-              if (j < 2) nxt[j].sc = A[a_sc + 64 * (2 * pp + 2 + j)];
-              const int t = 2 * pp + 2 + (j >= 4);
-              if (j == 2 || j == 4) nxt[j / 4].lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 2048 * t);
-              if (j == 3 || j == 5) nxt[j / 5].hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 2048 * t);
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[j][k][i] = v4f{0.f, 0.f, 0.f, 0.f};
+            asm volatile("" : "+a"(acc[j][k][i]));   // distinct registers from the start
+          }
+      AOp abuf[2];
+      v4i bw[2][4];   // weight operands of the stage: [unit k][row block i]
+      int bs[2][4];
+
+      // Operands of stage s's start: tile 0 and the weights.
+      auto read_start = [&](int s) __attribute__((always_inline)) {
+        if constexpr (NJ > 0) {
+          const lds_t* A = stage_buf(s);
+          abuf[0].sc = A[a_sc];
+          abuf[0].lo = *reinterpret_cast<const lds_v4i*>(A + a_lo);
+          abuf[0].hi = *reinterpret_cast<const lds_v4i*>(A + a_hi);
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              bw[k][i] = *reinterpret_cast<const lds_v4i*>(A + b_op + 4096 * k + 1024 * i);
+              bs[k][i] = A[b_sc + 256 * k + 64 * i];
             }
-            if ((j & 1) && q0 + (j >> 1) < q1) issue_load(q0 + (j >> 1), nw, s + 3);
-          }
-          // Keep this pair's MFMAs inside its condition (the compiler would
-          // otherwise sink them below the later pairs), in the order above.
+        }
+        asm volatile("" ::: "memory");
+      };
+      // Global load slot of MFMA m of tile j: with two or more tiles, the odd
+      // MFMAs of tiles 0 and 1 carry loads 0..3 and 4..6; with one tile,
+      // MFMAs 0..6 carry one each.
+      auto load_slot = [](int j, int m) constexpr -> int {
+        if (NJ == 1) return m < kLoadsPerStage ? m : -1;
+        if (j > 1 || !(m & 1)) return -1;
+        const int q = 4 * j + (m >> 1);
+        return q < kLoadsPerStage ? q : -1;
+      };
+      // One stage: per tile j, 8 MFMAs; after MFMAs 0..2 one read of tile
+      // j + 1's operands, and the global loads of stage s + 2 in their slots.
+      auto compute = [&](int s) __attribute__((always_inline)) {
+        const lds_t* A = stage_buf(s);
+        if constexpr (NJ == 0) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[2 * pp + h][i]));
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-            if (pp + 1 < 8 && j < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            if ((j & 1) && q0 + (j >> 1) < q1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, s + 2);
         } else {
+          auto tile_fn = [&](auto ji) __attribute__((always_inline)) {
+            constexpr int j = decltype(ji)::value;
+            AOp& cur = abuf[j & 1];
+            AOp& nxt = abuf[(j + 1) & 1];
 #pragma unroll
-          for (int q = q0; q < q1; ++q) issue_load(q, nw, s + 3);
+            for (int m = 0; m < 8; ++m) {
+              const int k = m >> 2, i = m & 3;
+              acc[j][k][i] = mfma_w4a8<0>(bw[k][i], cur.lo, cur.hi, acc[j][k][i], bs[k][i], cur.sc);
+              if constexpr (j + 1 < NJ) {
+                if (m == 0) nxt.sc = A[a_sc + 256 * (j + 1)];
+                if (m == 1) nxt.lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 8192 * (j + 1));
+                if (m == 2) nxt.hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 8192 * (j + 1));
+              }
+              if (load_slot(j, m) >= 0) issue_load(load_slot(j, m), s + 2);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+              if (j + 1 < NJ && m < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+              if (load_slot(j, m) >= 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+          };
+          static_for<0, NJ>(tile_fn);
         }
       };
-      static_for<0, 8>(pair_fn);
-    };
 
-    // After the stage-end wait the next stage's weights are in their
-    // registers: re-define them there so no use can move above the wait.
-    auto pin_w = [&](WStage& w) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(w.w[i]), "+v"(w.s[i]));
-    };
-    // Step s (set cur holds stage s's weights, nw takes stage s + 3's, next
-    // holds stage s + 1's): the stage's MFMAs and loads, then the wait for
-    // stage s + 1 (its 17 loads were issued two steps back, followed by the 17
-    // of each later step: 34), the barrier (stage s + 1 landed everywhere,
-    // stage s's buffer free), stage s + 1's first pair.
-    auto step = [&](const WStage& cur, WStage& nw, WStage& next, int s) __attribute__((always_inline)) {
-      compute(cur, nw, s);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");
-      asm volatile("s_barrier" ::: "memory");
-      pin_w(next);
-      const lds_t* An = stage_buf(s + 1);
-      read_a(buf[0][0], An, 0);
-      read_a(buf[0][1], An, 1);
+      for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, 0);
       asm volatile("" ::: "memory");
-    };
-    WStage w0, w1, w2, w3;
 #pragma unroll
-    for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, w0, 0);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, w1, 1);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, w2, 2);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWaitCount) : "memory");   // stage 0's loads
-    asm volatile("s_barrier" ::: "memory");
-    pin_w(w0);
-    {
-      const lds_t* A0 = stage_buf(0);
-      read_a(buf[0][0], A0, 0);
-      read_a(buf[0][1], A0, 1);
-    }
-    asm volatile("" ::: "memory");
-    // Stage loop, unrolled by 4 so each register set keeps a fixed name.
-    int s = 0;
-    for (; s + 4 <= n_stages; s += 4) {
-      step(w0, w3, w1, s);
-      step(w1, w0, w2, s + 1);
-      step(w2, w1, w3, s + 2);
-      step(w3, w2, w0, s + 3);
-    }
-    if (s < n_stages) step(w0, w3, w1, s);
-    if (s + 1 < n_stages) step(w1, w0, w2, s + 1);
-    if (s + 2 < n_stages) step(w2, w1, w3, s + 2);
-    // Drain the reloads issued past the end before the ring is reused.  The
-    // weight loads are asynchronous writes the compiler does not see: keep
-    // every register set allocated until they have landed, so none of them
-    // is handed to another value while a load into it is in flight.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    pin_w(w0);
-    pin_w(w1);
-    pin_w(w2);
-    pin_w(w3);
-    asm volatile("s_barrier" ::: "memory");
+      for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerStage) : "memory");   // stage 0's loads
+      asm volatile("s_barrier" ::: "memory");
+      read_start(0);
+      // Step s: the stage's MFMAs and loads, the wait for stage s + 1 (its
+      // loads were issued one step back, followed by this step's 7), the
+      // barrier (stage s + 1 landed everywhere, stage s's buffer free), and
+      // stage s + 1's first operands.
+      for (int s = 0; s < n_stages; ++s) {
+        compute(s);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerStage) : "memory");
+        asm volatile("s_barrier" ::: "memory");
+        if (s + 1 < n_stages) read_start(s + 1);
+      }
+      // Drain the reloads issued past the end before the ring is reused.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      asm volatile("s_barrier" ::: "memory");
 
-    auto pin = [&](auto tti) __attribute__((always_inline)) {
-      pin_acc_agpr(acc[decltype(tti)::value]);
-    };
-    static_for<0, 16>(pin);
-    auto epi = [&](auto tti) __attribute__((always_inline)) {
-      constexpr int tt = decltype(tti)::value;
-      if (2 * npairs > tt) {
-        const int t_in = tt * 16 + li;
-        store_subtile<FC1>(p, acc[tt], row_begin + t_in, t_in < n_valid, unit, g);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        pin_acc_agpr(acc[j][0]);
+        pin_acc_agpr(acc[j][1]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int t_in = 16 * (qt + 4 * j) + li;
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          store_subtile<FC1>(p, acc[j][k], row_begin + t_in, t_in < n_valid, 4 * cg + 2 * hw + k, g);
       }
     };
-    static_for<0, 16>(epi);
+    switch (nj) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
+    }
   }
 }
 
@@ -383,9 +409,12 @@ bool prefill_shape_ok(const FcParams& prm, bool fc1) {
   // groups of the tiled layout (I % 256); FC2: 256 output columns per tile,
   // whole 512-row groups (H % 512).  Buffer offsets are 32-bit: the
   // activation array and one expert's weights must each stay below 2 GiB.
+  // The expert metadata is kept in LDS: at most kMaxLdsExperts local experts.
+  // The restaged scales (K/32 bytes per grouped row) need 32-bit offsets too.
   const int64_t K = prm.K;
-  return K % kKS == 0 && (fc1 ? prm.I % 256 == 0 : prm.N % 512 == 0) &&
-         prm.act_rows * K < ((int64_t)1 << 31) && (int64_t)prm.N * (K / 2) < ((int64_t)1 << 31);
+  return K % kKS == 0 && (fc1 ? prm.I % 256 == 0 : prm.N % 512 == 0) && prm.E_local <= kMaxLdsExperts &&
+         prm.act_rows * K < ((int64_t)1 << 31) && (int64_t)prm.N * (K / 2) < ((int64_t)1 << 31) &&
+         prm.n_routes * (K / 32) < ((int64_t)1 << 31) && prm.act_st != nullptr;
 }
 
 hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* tile_prefix_all,
@@ -394,6 +423,13 @@ hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* 
   const int n_cg = fc1 ? prm.I / 128 : prm.N / kBN;
   // Persistent grid: one workgroup per CU, a multiple of the 8 XCDs.
   const int n_wg = (n_cu > 8 ? n_cu : 8) & ~7;
+  const int n_stages = prm.K / kKS;
+  const int R = (int)prm.n_routes;
+  if (R > 0) {
+    hipLaunchKernelGGL(stage_scales_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, prm.act_s,
+                       prm.K / 32, fc1 ? prm.gather : nullptr, prm.top_k, prm.expert_offsets,
+                       prm.E_local, R, n_stages, prm.act_st);
+  }
   const dim3 grid(n_wg), block(kThreads);
   if (fc1 && tiled)
     hipLaunchKernelGGL((fc_prefill_kernel<true, true>), grid, block, 0, stream, prm, n_cg);

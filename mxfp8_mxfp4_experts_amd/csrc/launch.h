@@ -17,16 +17,17 @@ hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, in
 hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
-                      uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all, int n_cu,
-                      bool tiled, hipStream_t stream);
+                      uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all,
+                      uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream);
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      float* y, const int32_t* tile_prefix_all, int n_cu, bool tiled,
-                      hipStream_t stream);
+                      float* y, const int32_t* tile_prefix_all, uint32_t* act_st, int n_cu,
+                      bool tiled, hipStream_t stream);
 struct FcParams;
 // Prefill-shaped FC kernels (fc_prefill.hip): usable when K % 128 == 0, the
 // weight rows split into whole 512-row groups and the operands fit 32-bit
-// buffer offsets.  They read the 256-row tile prefix.
+// buffer offsets.  They read the 256-row tile prefix, and first restage the
+// input's scale dwords into prm.act_st (stage-major, grouped-row order).
 bool prefill_shape_ok(const FcParams& prm, bool fc1);
 hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* tile_prefix_all,
                              int n_cu, hipStream_t stream);
