@@ -208,12 +208,13 @@ static moe_status_t fc2_impl(const uint8_t* hq, const uint8_t* hs, int T, int H,
   if (s != MOE_OK) return s;
   char* ws = static_cast<char*>(workspace);
   const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + l.tile_prefix);
-  float* y = reinterpret_cast<float*>(ws + l.y);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + l.y);
+  int8_t* ye = reinterpret_cast<int8_t*>(ws + l.ye);
   uint32_t* act_st = reinterpret_cast<uint32_t*>(ws + l.act_st);
-  hipError_t e = launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, prefix,
-                            act_st, n_cu, tiled, stream);
+  hipError_t e = launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, ye,
+                            prefix, act_st, n_cu, tiled, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return finish(launch_combine(y, H, route_row, topk_w, T, top_k, out, ld_out, stream));
+  return finish(launch_combine(y, ye, H, route_row, topk_w, T, top_k, out, ld_out, stream));
 }
 
 moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,

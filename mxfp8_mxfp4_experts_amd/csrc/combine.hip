@@ -2,7 +2,8 @@
 // finalize step after GEMM2; "对称性约束": the non-fused, deterministic
 // finalize).  out[t] = bf16 of the sum over kept slots k, in slot order, of
 // w[t,k] * y[route_row[t,k]], accumulated in float32; masked and dropped
-// slots contribute nothing, and a token with no kept slot gets zeros.
+// slots contribute nothing, and a token with no kept slot gets zeros.  The
+// FC2 rows arrive as fp16 with a power-of-two scale per 64 columns.
 #include "common.h"
 #include "fc_common.h"
 #include "launch.h"
@@ -11,8 +12,10 @@ namespace mi355moe {
 
 namespace {
 
-// out[t] = bf16( sum over kept k, in k order, of w[t,k] * y[route_row[t,k]] ).
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int H,
+// out[t] = bf16( sum over kept k, in k order, of w[t,k] * y[route_row[t,k]] ),
+// with y = fp16 row * 2^ye.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int8_t* __restrict__ ye, int H,
                                                       const int32_t* __restrict__ route_row,
                                                       const float* __restrict__ topk_w, int T,
                                                       int K, uint16_t* __restrict__ out,
@@ -34,24 +37,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       rr[j] = k < K ? route_row[(size_t)t * K + k] : -1;
       wk[j] = k < K ? topk_w[(size_t)t * K + k] : 0.0f;
     }
-    v4f a[16], b[16];
+    uint4 a[16];
+    int ex[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      a[j] = v4f{0.f, 0.f, 0.f, 0.f};
-      b[j] = a[j];
+      a[j] = uint4{0u, 0u, 0u, 0u};
+      ex[j] = 0;
       if (rr[j] >= 0) {
-        const v4f* src = reinterpret_cast<const v4f*>(y + (size_t)rr[j] * H + (size_t)c * 8);
-        a[j] = src[0];
-        b[j] = src[1];
+        a[j] = *reinterpret_cast<const uint4*>(y + (size_t)rr[j] * H + (size_t)c * 8);
+        ex[j] = ye[(size_t)rr[j] * (H / 64) + (c >> 3)];
       }
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       if (rr[j] < 0) continue;
+      const uint32_t h[4] = {a[j].x, a[j].y, a[j].z, a[j].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i] = fmaf(wk[j], a[j][i], acc[i]);
-        acc[4 + i] = fmaf(wk[j], b[j][i], acc[4 + i]);
+        const float lo = ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(h[i] & 0xFFFF)), ex[j]);
+        const float hi = ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)(h[i] >> 16)), ex[j]);
+        acc[2 * i] = fmaf(wk[j], lo, acc[2 * i]);
+        acc[2 * i + 1] = fmaf(wk[j], hi, acc[2 * i + 1]);
       }
     }
   }
@@ -65,12 +71,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,
-                          int T, int K, uint16_t* out, int64_t ld_out, hipStream_t stream) {
+hipError_t launch_combine(const uint16_t* y, const int8_t* ye, int H, const int32_t* route_row,
+                          const float* topk_w, int T, int K, uint16_t* out, int64_t ld_out,
+                          hipStream_t stream) {
   const int64_t threads = (int64_t)T * (H / 8);
   const int blocks = (int)((threads + 255) / 256);
-  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, y, H, route_row, topk_w,
-                     T, K, out, ld_out);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, stream, y, ye, H, route_row,
+                     topk_w, T, K, out, ld_out);
   return hipGetLastError();
 }
 

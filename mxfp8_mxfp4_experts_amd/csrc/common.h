@@ -35,7 +35,8 @@ struct WsLayout {
   size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
   size_t act_st;        // uint32 [max(H, I) / 128][T * top_k]: an FC input's scale dwords,
                         // stage-major in grouped-row order (prefill-shaped FC kernels)
-  size_t y;             // float [T * top_k][H]  (FC2 rows before the combine)
+  size_t y;             // fp16 [T * top_k][H]  (FC2 rows before the combine, scaled)
+  size_t ye;            // int8 [T * top_k][H / 64]: power-of-two scale of each 64 columns
   size_t total;
 };
 
@@ -51,7 +52,9 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I) {
   l.act_st = off;
   off = align256(off + (size_t)T * top_k * (size_t)((H > I ? H : I) / 32));
   l.y = off;
-  off = align256(off + sizeof(float) * (size_t)T * top_k * H);
+  off = align256(off + sizeof(uint16_t) * (size_t)T * top_k * H);
+  l.ye = off;
+  off = align256(off + (size_t)T * top_k * (H / 64));
   l.total = off;
   return l;
 }

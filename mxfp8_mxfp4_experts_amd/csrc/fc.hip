@@ -275,15 +275,15 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
 
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      float* y, const int32_t* tile_prefix_all, uint32_t* act_st, int n_cu,
-                      bool tiled, hipStream_t stream) {
+                      uint16_t* y, int8_t* ye, const int32_t* tile_prefix_all,
+                      uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream) {
   FcParams p{};
   p.act = hq; p.act_s = hs; p.act_rows = (int64_t)T * top_k; p.gather = nullptr; p.top_k = top_k;
   p.n_routes = (int64_t)T * top_k; p.act_st = act_st;
   p.w = w2; p.w_s = w2_s; p.K = I; p.N = H; p.I = I;
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = H / 64;
-  p.y = y;
+  p.y = y; p.ye = ye;
   return launch_fc<false>(p, T * top_k, tile_prefix_all, n_cu, tiled, stream);
 }
 

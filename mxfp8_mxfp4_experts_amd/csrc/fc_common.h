@@ -36,7 +36,8 @@ struct FcParams {
   float alpha, beta;
   uint8_t* hq;               // FC1 out [R, I]
   uint8_t* hs;               // FC1 out [R, I/32]
-  float* y;                  // FC2 out [R, N]
+  uint16_t* y;               // FC2 out [R, N]: fp16 of y / 2^ye
+  int8_t* ye;                // FC2 out [R, N / 64]: scale exponent per 64 columns
 };
 
 // SiTU(g, u) = alpha tanh(g / alpha) sigmoid(g) * beta tanh(u / beta)
@@ -159,10 +160,33 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
       if (g == 0) p.hs[(size_t)row * (p.I / 32) + c0 / 32] = (uint8_t)(ex + 127);
     }
   } else {
-    if (valid) {
-      float* dst = p.y + (size_t)row * p.N + u * 64 + 4 * g;
+    // The 64 columns of the unit for this row (16 values in each of the four
+    // lanes with this li) share one power-of-two scale 2^e chosen so that the
+    // largest finite magnitude lands in [2^14, 2^15): fp16 keeps every value
+    // to 2^-11 relative (non-finite values stay non-finite).
+    float amax = 0.0f;
 #pragma unroll
-      for (int bk = 0; bk < 4; ++bk) *reinterpret_cast<v4f*>(dst + 16 * bk) = acc[bk];
+    for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = fabsf(acc[bk][r]);
+        amax = (v <= 3.4028235e38f && v > amax) ? v : amax;   // finite values only
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int fe = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    const int e = fe - 141 < -128 ? -128 : fe - 141;
+    if (valid) {
+      uint16_t* dst = p.y + (size_t)row * p.N + u * 64 + 4 * g;
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk) {
+        uint32_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          h[r] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(acc[bk][r], -e));
+        *reinterpret_cast<uint2*>(dst + 16 * bk) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      }
+      if (g == 0) p.ye[(size_t)row * (p.N / 64) + u] = (int8_t)e;
     }
   }
 }

@@ -21,8 +21,8 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
                       uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream);
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      float* y, const int32_t* tile_prefix_all, uint32_t* act_st, int n_cu,
-                      bool tiled, hipStream_t stream);
+                      uint16_t* y, int8_t* ye, const int32_t* tile_prefix_all,
+                      uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream);
 struct FcParams;
 // Prefill-shaped FC kernels (fc_prefill.hip): usable when K % 128 == 0, the
 // weight rows split into whole 512-row groups and the operands fit 32-bit
@@ -34,7 +34,8 @@ hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* 
 // One-time reordering of checkpoint-layout weights into the tiled layout.
 hipError_t launch_prepack(bool fc1, const uint8_t* w, const uint8_t* ws, int E_local, int N,
                           int K, int I, uint8_t* tw, uint8_t* tws, hipStream_t stream);
-hipError_t launch_combine(const float* y, int H, const int32_t* route_row, const float* topk_w,
-                          int T, int K, uint16_t* out, int64_t ld_out, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* y, const int8_t* ye, int H, const int32_t* route_row,
+                          const float* topk_w, int T, int K, uint16_t* out, int64_t ld_out,
+                          hipStream_t stream);
 
 }  // namespace mi355moe
