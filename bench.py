@@ -157,11 +157,14 @@ def main():
     hq, hs = layer.hq[:R], layer.hs[:R]
 
     def step(ev=None):
-        if not given:
-            B.moe_route(logits, bias, K, cfg.routed_scaling, idx, tw)
-        B.moe_quant_mxfp8(x, xq, xs)
-        B.moe_permute(idx, cfg.expert_offset, E_local, layer.workspace, layer.expert_offsets,
-                      sroute, rrow)
+        if given:
+            B.moe_quant_mxfp8(x, xq, xs)
+            B.moe_permute(idx, cfg.expert_offset, E_local, layer.workspace, layer.expert_offsets,
+                          sroute, rrow)
+        else:
+            B.moe_route_quant_permute(logits, bias, K, cfg.routed_scaling, x, cfg.expert_offset,
+                                      E_local, layer.workspace, idx, tw, xq, xs,
+                                      layer.expert_offsets, sroute, rrow)
         if ev is not None:
             ev[0].record()
         B.moe_fc1_situ(xq, xs, K, layer.expert_offsets, sroute, layer.w13, layer.w13_s,

@@ -3,7 +3,8 @@
  * Instinct MI355X (gfx950).
  *
  * The layer (one GPU's share of a Kimi-K3-style routed-expert MoE) is five
- * calls, issued in this order on one HIP stream:
+ * calls, issued in this order on one HIP stream (the first three can also be
+ * issued as one, moe_route_quant_permute):
  *
  *   moe_route        sigmoid + correction-bias top-k routing, renormalised weights
  *   moe_quant_mxfp8  bf16 activations -> MXFP8 (E4M3 + one E8M0 scale per 32)
@@ -130,6 +131,23 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int top_k, int expert_o
                          int32_t* route_row, void* workspace, size_t ws_bytes,
                          hipStream_t stream);
 
+/* a1 + a2 + a3 in one call (decode latency: page 1 "Serving call chain" runs
+ * routing, quantisation and grouping before the expert GEMMs; their fixed
+ * launch costs are a visible share of a decode step).  Computes exactly what
+ * moe_route, then moe_quant_mxfp8, then moe_permute compute with the same
+ * arguments (same bytes in every output and in the workspace), and accepts
+ * what those three accept together (every check of each; xs needs only
+ * 4-byte alignment as in moe_quant_mxfp8).  For T <= 16, E <= 1024 and small
+ * enough E_local it is a single launch; otherwise it issues the three
+ * launches in order on `stream`. */
+moe_status_t moe_route_quant_permute(const float* logits, int64_t ld_logits, const float* bias,
+                                     int T, int E, int top_k, float routed_scaling,
+                                     const uint16_t* x, int64_t ld_x, int H, int expert_offset,
+                                     int E_local, int32_t* topk_idx, float* topk_w, uint8_t* xq,
+                                     uint8_t* xs, int32_t* expert_offsets, int32_t* sorted_route,
+                                     int32_t* route_row, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream);
+
 /* a4 + a5 + a6 -- FC1 grouped GEMM, SiTU, requantisation (page 1 "Serving call
  * chain": grouped GEMM1 then gated activation; "Real checkpoint contract": w13
  * holds [gate; up] in two contiguous halves, SiTU gate' = alpha *
@@ -163,7 +181,9 @@ moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, in
  *                   topk_w[t,k] * y[route_row[t,k]] ) with float accumulation;
  *                   a token with no kept slot gets zeros.  Bitwise
  *                   deterministic.
- *   workspace       the buffer moe_permute filled (holds y [T*top_k, H] float). */
+ *   workspace       the buffer moe_permute filled (holds the per-route FC2 rows
+ *                   y [T*top_k, H] as fp16 of y / 2^e with one exponent e per
+ *                   64 columns: 2^-11 relative, below the output's bf16 step). */
 moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                              int top_k, int E_local, const int32_t* expert_offsets,
                              const int32_t* route_row, const float* topk_w,

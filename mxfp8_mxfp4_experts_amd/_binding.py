@@ -26,7 +26,7 @@ MOE_STATUS = {
 EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_route", "moe_quant_mxfp8",
     "moe_permute", "moe_fc1_situ", "moe_fc2_combine", "moe_prepack_w13", "moe_prepack_w2",
-    "moe_fc1_situ_tiled", "moe_fc2_combine_tiled",
+    "moe_fc1_situ_tiled", "moe_fc2_combine_tiled", "moe_route_quant_permute",
 )
 
 _P = ctypes.c_void_p
@@ -54,6 +54,9 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.moe_quant_mxfp8.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
     lib.moe_permute.restype = _I
     lib.moe_permute.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_route_quant_permute.restype = _I
+    lib.moe_route_quant_permute.argtypes = [_P, _I64, _P, _I, _I, _I, _F, _P, _I64, _I, _I, _I,
+                                            _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.moe_fc1_situ.restype = _I
     lib.moe_fc1_situ.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _P, _P, _P,
                                  _SZ, _P]
@@ -173,6 +176,53 @@ def moe_quant_mxfp8(x: torch.Tensor, xq: Optional[torch.Tensor] = None,
     _check("moe_quant_mxfp8", lib().moe_quant_mxfp8(_ptr(xb), x.stride(0), T, H, _ptr(xq),
                                                     _ptr(xs), _stream()))
     return xq, xs
+
+
+def moe_route_quant_permute(logits: torch.Tensor, bias: Optional[torch.Tensor], top_k: int,
+                            routed_scaling: float, x: torch.Tensor, expert_offset: int,
+                            E_local: int, workspace: torch.Tensor, topk_idx=None, topk_w=None,
+                            xq=None, xs=None, expert_offsets=None, sorted_route=None,
+                            route_row=None):
+    """moe_route, moe_quant_mxfp8 and moe_permute as one call (same results)."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [T, E] with unit column stride")
+    _need(logits, "logits", torch.float32, contiguous=False)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [T, H] with unit column stride")
+    xb = x if x.dtype == torch.uint16 else (x.view(torch.uint16) if x.dtype == torch.bfloat16 else None)
+    if xb is None:
+        raise ValueError(f"x must be bfloat16 (or uint16 bf16 bits), got {x.dtype}")
+    _need(xb, "x", torch.uint16, contiguous=False)
+    T, E = logits.shape
+    H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x and logits must have the same number of rows")
+    dev = logits.device
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,), device=dev)
+    R = T * top_k
+    topk_idx = torch.empty((T, top_k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_w = torch.empty((T, top_k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev) if xq is None else xq
+    xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev) if xs is None else xs
+    if expert_offsets is None:
+        expert_offsets = torch.empty(E_local + 1, dtype=torch.int32, device=dev)
+    sorted_route = torch.empty(R, dtype=torch.int32, device=dev) if sorted_route is None else sorted_route
+    route_row = torch.empty(R, dtype=torch.int32, device=dev) if route_row is None else route_row
+    _need(topk_idx, "topk_idx", torch.int32, (T, top_k), device=dev)
+    _need(topk_w, "topk_w", torch.float32, (T, top_k), device=dev)
+    _need(xq, "xq", torch.uint8, (T, H), device=dev)
+    _need(xs, "xs", torch.uint8, (T, H // 32), device=dev)
+    _need(expert_offsets, "expert_offsets", torch.int32, (E_local + 1,), device=dev)
+    _need(sorted_route, "sorted_route", torch.int32, (R,), device=dev)
+    _need(route_row, "route_row", torch.int32, (R,), device=dev)
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    _check("moe_route_quant_permute", lib().moe_route_quant_permute(
+        _ptr(logits), logits.stride(0), _ptr(bias), T, E, top_k, float(routed_scaling), _ptr(xb),
+        x.stride(0), H, expert_offset, E_local, _ptr(topk_idx), _ptr(topk_w), _ptr(xq), _ptr(xs),
+        _ptr(expert_offsets), _ptr(sorted_route), _ptr(route_row), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return topk_idx, topk_w, xq, xs, expert_offsets, sorted_route, route_row
 
 
 def moe_permute(topk_idx: torch.Tensor, expert_offset: int, E_local: int, workspace: torch.Tensor,

@@ -1,0 +1,86 @@
+// a1 + a2 + a3 in one launch, for decode-sized batches (page 1, "Serving call
+// chain": routing, activation quantisation and the expert grouping run before
+// the expert GEMMs; the fixed launch costs of these small steps are a visible
+// share of a decode step).
+//
+// Workgroup 0 routes every token and then groups the routes: its sixteen
+// wavefronts first compute all T x E selection keys into LDS, then wavefront
+// t selects token t's experts (select_topk_wave, exactly as the routing
+// kernel does), keeping the ids in LDS, and after a barrier the whole
+// workgroup runs the single-workgroup grouping (permute_block) on them.  The
+// other workgroups quantise the activations meanwhile (quant_piece), so the
+// launch takes about as long as the routing alone.  The results are the bytes
+// the three separate calls produce.
+#include "common.h"
+#include "launch.h"
+#include "permute_dev.h"
+#include "quant_dev.h"
+#include "route_dev.h"
+
+namespace mi355moe {
+
+namespace {
+
+__global__ __launch_bounds__(kPermThreads) void front_kernel(
+    const float* __restrict__ logits, int64_t ld, const float* __restrict__ bias, int T, int E,
+    int K, float scaling, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    const uint16_t* __restrict__ x, int64_t ld_x, int H, uint8_t* __restrict__ xq,
+    uint8_t* __restrict__ xs, int offset, int E_local, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ sorted_route, int32_t* __restrict__ route_row,
+    int32_t* __restrict__ tile_prefix) {
+  if (blockIdx.x > 0) {
+    quant_piece(x, ld_x, T, H, xq, xs, (int64_t)(blockIdx.x - 1) * kPermThreads + threadIdx.x);
+    return;
+  }
+  extern __shared__ int lds_i[];
+  uint32_t* keys = reinterpret_cast<uint32_t*>(lds_i);   // [T][E]
+  int* ids = lds_i + T * E;                              // [T * K]
+  int* cnt = ids + T * K;                                // [E_local]
+  int* cursor = cnt + E_local;                           // [E_local]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < T * E; i += kPermThreads) {
+    const int t = i / E, e = i - t * E;
+    keys[i] = ordered_key(sigmoid_score(logits[(size_t)t * ld + e]) + (bias ? bias[e] : 0.0f));
+  }
+  __syncthreads();
+  if (wave < T) {
+    int id;
+    float w;
+    select_topk_wave(keys + wave * E, logits + (size_t)wave * ld, E, K, scaling, lane, id, w);
+    if (lane < K) {
+      topk_idx[(size_t)wave * K + lane] = id;
+      topk_w[(size_t)wave * K + lane] = w;
+      ids[wave * K + lane] = id;
+    }
+  }
+  __syncthreads();
+  permute_block([&](int r) { return ids[r]; }, T * K, offset, E_local, expert_offsets,
+                sorted_route, route_row, tile_prefix, cnt, cursor);
+}
+
+size_t front_lds_bytes(int T, int E, int K, int E_local) {
+  return sizeof(int) * ((size_t)T * E + (size_t)T * K + 2 * (size_t)E_local);
+}
+
+}  // namespace
+
+bool front_fusable(int T, int E, int K, int E_local) {
+  return T >= 1 && T <= kPermWaves && E <= 64 * kRegExpertsPerLane &&
+         front_lds_bytes(T, E, K, E_local) <= 64 * 1024;
+}
+
+hipError_t launch_front(const float* logits, int64_t ld, const float* bias, int T, int E, int K,
+                        float scaling, int32_t* topk_idx, float* topk_w, const uint16_t* x,
+                        int64_t ld_x, int H, uint8_t* xq, uint8_t* xs, int offset, int E_local,
+                        int32_t* offs, int32_t* sorted_route, int32_t* route_row,
+                        int32_t* tile_prefix, hipStream_t stream) {
+  const int64_t pieces = (int64_t)T * (H / 8);
+  const int blocks = 1 + (int)((pieces + kPermThreads - 1) / kPermThreads);
+  hipLaunchKernelGGL(front_kernel, dim3(blocks), dim3(kPermThreads),
+                     front_lds_bytes(T, E, K, E_local), stream, logits, ld, bias, T, E, K, scaling,
+                     topk_idx, topk_w, x, ld_x, H, xq, xs, offset, E_local, offs, sorted_route,
+                     route_row, tile_prefix);
+  return hipGetLastError();
+}
+
+}  // namespace mi355moe

@@ -14,6 +14,15 @@ hipError_t launch_quant(const uint16_t* x, int64_t ld, int T, int H, uint8_t* xq
 hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, int32_t* offs,
                           int32_t* sorted_route, int32_t* route_row, int32_t* tile_prefix,
                           int32_t* counts, hipStream_t stream);
+// Route + quantise + group in one launch (front.hip), for batches that
+// front_fusable accepts (T <= 16, E <= 1024, its LDS within 64 KB); the same
+// bytes as launch_route, launch_quant and launch_permute.
+bool front_fusable(int T, int E, int K, int E_local);
+hipError_t launch_front(const float* logits, int64_t ld, const float* bias, int T, int E, int K,
+                        float scaling, int32_t* topk_idx, float* topk_w, const uint16_t* x,
+                        int64_t ld_x, int H, uint8_t* xq, uint8_t* xs, int offset, int E_local,
+                        int32_t* offs, int32_t* sorted_route, int32_t* route_row,
+                        int32_t* tile_prefix, hipStream_t stream);
 hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,

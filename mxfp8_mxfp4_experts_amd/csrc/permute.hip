@@ -9,147 +9,29 @@
 // sorted_route[row] = route, route_row[route] = row or -1; grouped rows past
 // the kept count hold -1; tile prefixes for the FC tile heights 16..256.
 //
-// Small batches: one workgroup of 1024 threads
-//  1. histogram of local expert ids in LDS;
-//  2. block-wide exclusive scans of the counts and of the per-expert tile
-//     counts for the FC tile heights 16, 32, 64, 128 and 256 rows;
-//  3. one wavefront walks the routes in ascending order, 64 at a time:
-//     lanes with the same expert find each other with ballots over the id
-//     bits, the lowest such lane reserves their rows from the expert's LDS
-//     cursor, and each lane takes base + its rank among them.  This keeps
-//     the (token, slot) order inside every expert.
+// Small batches: one workgroup runs permute_block (permute_dev.h): a
+// histogram in LDS, block-wide scans of the counts and tile counts, then one
+// wavefront ranks the routes 64 at a time with ballots over the id bits.
 // Large batches: the routes are cut into chunks (perm_chunk_size); a count
 // kernel writes each chunk's histogram, one workgroup turns the histograms
 // into expert offsets, tile prefixes and each chunk's first row per expert,
-// and a rank kernel (one wavefront per chunk) runs step 3 on its chunk from
+// and a rank kernel (one wavefront per chunk) runs the ballot ranking on its chunk from
 // those starting rows.
 #include "common.h"
 #include "launch.h"
+#include "permute_dev.h"
 
 namespace mi355moe {
 
 namespace {
-
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / 64;
-constexpr int kScanVals = 1 + kNumTileSizes;
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t* __restrict__ idx, int R, int offset, int E_local,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_route,
     int32_t* __restrict__ route_row, int32_t* __restrict__ tile_prefix) {
   extern __shared__ int lds_i[];
-  int* cnt = lds_i;              // [E_local]
-  int* cursor = lds_i + E_local; // [E_local]
-  __shared__ int wave_tot[kPermWaves][kScanVals];
-  __shared__ int n_kept_s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  for (int e = tid; e < E_local; e += kPermThreads) cnt[e] = 0;
-  __syncthreads();
-  for (int r = tid; r < R; r += kPermThreads) {
-    int g = idx[r];
-    int l = g - offset;
-    if (g >= 0 && l >= 0 && l < E_local) atomicAdd(&cnt[l], 1);
-  }
-  __syncthreads();
-
-  // Each thread owns a contiguous run of experts.
-  const int per = (E_local + kPermThreads - 1) / kPermThreads;
-  const int e0 = tid * per;
-  int local[kScanVals];
-#pragma unroll
-  for (int v = 0; v < kScanVals; ++v) local[v] = 0;
-  for (int e = e0; e < e0 + per && e < E_local; ++e) {
-    int c = cnt[e];
-    local[0] += c;
-#pragma unroll
-    for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += (c + (16 << i) - 1) >> (4 + i);
-  }
-  // Inclusive wave scan, then scan of wave totals.
-  int incl[kScanVals];
-#pragma unroll
-  for (int v = 0; v < kScanVals; ++v) {
-    int x = local[v];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      int y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    incl[v] = x;
-    if (lane == 63) wave_tot[wave][v] = x;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run[kScanVals];
-    for (int v = 0; v < kScanVals; ++v) run[v] = 0;
-    for (int w = 0; w < kPermWaves; ++w)
-      for (int v = 0; v < kScanVals; ++v) {
-        int x = wave_tot[w][v];
-        wave_tot[w][v] = run[v];
-        run[v] += x;
-      }
-    n_kept_s = run[0];
-    expert_offsets[E_local] = run[0];
-    for (int i = 0; i < kNumTileSizes; ++i) tile_prefix[i * (E_local + 1) + E_local] = run[1 + i];
-  }
-  __syncthreads();
-  int excl[kScanVals];
-#pragma unroll
-  for (int v = 0; v < kScanVals; ++v) excl[v] = incl[v] - local[v] + wave_tot[wave][v];
-  for (int e = e0; e < e0 + per && e < E_local; ++e) {
-    int c = cnt[e];
-    expert_offsets[e] = excl[0];
-    cursor[e] = excl[0];
-    excl[0] += c;
-#pragma unroll
-    for (int i = 0; i < kNumTileSizes; ++i) {
-      tile_prefix[i * (E_local + 1) + e] = excl[1 + i];
-      excl[1 + i] += (c + (16 << i) - 1) >> (4 + i);
-    }
-  }
-  __syncthreads();
-  const int n_kept = n_kept_s;
-  for (int r = n_kept + tid; r < R; r += kPermThreads) sorted_route[r] = -1;
-
-  if (wave == 0) {
-    int nbits = 0;
-    while ((1 << nbits) < E_local) ++nbits;
-    for (int base = 0; base < R; base += 64) {
-      const int r = base + lane;
-      int l = -1;
-      if (r < R) {
-        int g = idx[r];
-        int ll = g - offset;
-        if (g >= 0 && ll >= 0 && ll < E_local) l = ll;
-      }
-      const bool kept = l >= 0;
-      uint64_t peers = __ballot(kept);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const bool set = kept && ((l >> bit) & 1);
-        const uint64_t m = __ballot(set);
-        peers &= set ? m : ~m;
-      }
-      const uint64_t lower = lane ? (~0ull >> (64 - lane)) : 0ull;
-      const int rank = __popcll(peers & lower);
-      const int leader = kept ? (__ffsll((long long)peers) - 1) : lane;
-      int start = 0;
-      if (kept && leader == lane) {
-        start = cursor[l];
-        cursor[l] = start + __popcll(peers);
-      }
-      start = __shfl(start, leader);
-      if (r < R) {
-        if (kept) {
-          const int pos = start + rank;
-          sorted_route[pos] = r;
-          route_row[r] = pos;
-        } else {
-          route_row[r] = -1;
-        }
-      }
-    }
-  }
+  permute_block([&](int r) { return idx[r]; }, R, offset, E_local, expert_offsets, sorted_route,
+                route_row, tile_prefix, lds_i, lds_i + E_local);
 }
 
 // Local expert of route r, or -1 (masked slot or outside the window).

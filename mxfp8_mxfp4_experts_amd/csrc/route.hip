@@ -17,54 +17,14 @@
 //    restricted to keys below the previous winner.
 #include "common.h"
 #include "launch.h"
+#include "route_dev.h"
 
 namespace mi355moe {
 
 namespace {
 
-__device__ __forceinline__ uint32_t ordered_key(float f) {
-  uint32_t b = __float_as_uint(f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
 constexpr int kRouteWaves = 4;
 
-// Sigmoid evaluated in double and rounded once to float.  Used for both the
-// selection keys and the selected scores, so the two agree bit for bit.
-__device__ __forceinline__ float sigmoid_score(float logit) {
-  return (float)(1.0 / (1.0 + exp(-(double)logit)));
-}
-
-__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
-
-// Wavefront maximum / minimum of an unsigned value, uniform result: inclusive
-// scans within 16-lane rows (row_shr 1, 2, 4, 8), then row_bcast 15 and 31
-// carry the rows' results up to lane 63.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
-  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
-  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
-  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
-  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
-  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xf, 0xf, false));
-  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xf, 0xf, false));
-  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false));
-  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false));
-  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false));
-  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-constexpr int kRegExpertsPerLane = 16;   // register path: E <= 1024
-
-// One workgroup per token: its four wavefronts compute the keys (the double
-// precision sigmoid is the costly part) into LDS, then the first wavefront
-// selects.
 __global__ __launch_bounds__(256) void route_reg_kernel(
     const float* __restrict__ logits, int64_t ld, const float* __restrict__ bias, int T, int E,
     int K, float scaling, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
@@ -76,35 +36,12 @@ __global__ __launch_bounds__(256) void route_reg_kernel(
   __syncthreads();
   if (threadIdx.x >= 64) return;                     // whole wavefronts leave
   const int lane = threadIdx.x;
-  uint32_t key[kRegExpertsPerLane];
-  uint32_t avail = 0;                                // bit j: expert lane + 64 j not yet taken
-#pragma unroll
-  for (int j = 0; j < kRegExpertsPerLane; ++j) {
-    const int e = lane + 64 * j;
-    key[j] = e < E ? keys_s[e] : 0u;
-    avail |= (e < E ? 1u : 0u) << j;
-  }
-  int my_id = 0;
-  for (int k = 0; k < K; ++k) {
-    uint32_t best = 0, best_e = 0xFFFFFFFFu;
-#pragma unroll
-    for (int j = 0; j < kRegExpertsPerLane; ++j) {
-      const bool take = ((avail >> j) & 1u) && (best_e == 0xFFFFFFFFu || key[j] > best);
-      best = take ? key[j] : best;
-      best_e = take ? (uint32_t)(lane + 64 * j) : best_e;
-    }
-    const uint32_t m = wave_max_u32(best);
-    const uint32_t win = wave_min_u32(best == m ? best_e : 0xFFFFFFFFu);   // < E: K <= E
-    if ((int)(win & 63) == lane) avail &= ~(1u << (win >> 6));
-    if (lane == k) my_id = (int)win;
-  }
-  my_id = (my_id >= 0 && my_id < E) ? my_id : 0;
-  float my_s = lane < K ? sigmoid_score(row[my_id]) : 0.0f;
-  double total = 0.0;
-  for (int k = 0; k < K; ++k) total += (double)__shfl(my_s, k);   // left to right
+  int id;
+  float w;
+  select_topk_wave(keys_s, row, E, K, scaling, lane, id, w);
   if (lane < K) {
-    topk_idx[(size_t)t * K + lane] = my_id;
-    topk_w[(size_t)t * K + lane] = (float)(((double)my_s / total) * (double)scaling);
+    topk_idx[(size_t)t * K + lane] = id;
+    topk_w[(size_t)t * K + lane] = w;
   }
 }
 

@@ -1,0 +1,91 @@
+// Routing pieces shared by the routing kernels (route.hip) and the fused
+// route + quantise + group launch (front.hip).
+//
+// Page 1, "Serving call chain" and "Key sources" table (routing row): sigmoid
+// scores, the correction bias only takes part in choosing experts, the weights
+// gather the bias-free scores and are normalised; page 5: routed scaling.
+#pragma once
+
+#include "common.h"
+
+namespace mi355moe {
+
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Sigmoid evaluated in double and rounded once to float.  Used for both the
+// selection keys and the selected scores, so the two agree bit for bit.
+__device__ __forceinline__ float sigmoid_score(float logit) {
+  return (float)(1.0 / (1.0 + exp(-(double)logit)));
+}
+
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+// Wavefront maximum / minimum of an unsigned value, uniform result: inclusive
+// scans within 16-lane rows (row_shr 1, 2, 4, 8), then row_bcast 15 and 31
+// carry the rows' results up to lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xf, 0xf, false));
+  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xf, 0xf, false));
+  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false));
+  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false));
+  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false));
+  v = umin32(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+constexpr int kRegExpertsPerLane = 16;   // register path: E <= 1024
+
+// One wavefront selects the top K of one token (E <= 64 * kRegExpertsPerLane)
+// from its keys in LDS.  Lane l holds the keys of experts l, l + 64, ...; each
+// of the K rounds takes the lane's best remaining key, the wavefront maximum of
+// those (DPP row shifts and broadcasts), then the smallest expert index among
+// the lanes holding that maximum; the owning lane retires the winner.  Lane
+// k < K returns slot k's expert and weight (s_k / sum_j s_j in double, times
+// scaling).  Every lane must call this.
+__device__ __forceinline__ void select_topk_wave(const uint32_t* keys_s, const float* row, int E,
+                                                 int K, float scaling, int lane, int& id_out,
+                                                 float& w_out) {
+  uint32_t key[kRegExpertsPerLane];
+  uint32_t avail = 0;                                // bit j: expert lane + 64 j not yet taken
+#pragma unroll
+  for (int j = 0; j < kRegExpertsPerLane; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? keys_s[e] : 0u;
+    avail |= (e < E ? 1u : 0u) << j;
+  }
+  int my_id = 0;
+  for (int k = 0; k < K; ++k) {
+    uint32_t best = 0, best_e = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < kRegExpertsPerLane; ++j) {
+      const bool take = ((avail >> j) & 1u) && (best_e == 0xFFFFFFFFu || key[j] > best);
+      best = take ? key[j] : best;
+      best_e = take ? (uint32_t)(lane + 64 * j) : best_e;
+    }
+    const uint32_t m = wave_max_u32(best);
+    const uint32_t win = wave_min_u32(best == m ? best_e : 0xFFFFFFFFu);   // < E: K <= E
+    if ((int)(win & 63) == lane) avail &= ~(1u << (win >> 6));
+    if (lane == k) my_id = (int)win;
+  }
+  my_id = (my_id >= 0 && my_id < E) ? my_id : 0;
+  const float my_s = lane < K ? sigmoid_score(row[my_id]) : 0.0f;
+  double total = 0.0;
+  for (int k = 0; k < K; ++k) total += (double)__shfl(my_s, k);   // left to right
+  id_out = my_id;
+  w_out = (float)(((double)my_s / total) * (double)scaling);
+}
+
+}  // namespace mi355moe

@@ -64,15 +64,20 @@ class MoELayer:
         if T > self.max_tokens:
             self._alloc(T)
         K = self.top_k
+        R = T * K
         idx, w = self.topk_idx[:T], self.topk_w[:T]
+        xq, xs = self.xq[:T], self.xs[:T]
         if topk_idx is None:
-            B.moe_route(logits, bias, K, self.routed_scaling, idx, w)
+            # routing, quantisation and grouping as one call
+            B.moe_route_quant_permute(logits, bias, K, self.routed_scaling, x, self.expert_offset,
+                                      self.E_local, self.workspace, idx, w, xq, xs,
+                                      self.expert_offsets, self.sorted_route[:R],
+                                      self.route_row[:R])
         else:
             idx, w = topk_idx, topk_w
-        xq, xs = B.moe_quant_mxfp8(x, self.xq[:T], self.xs[:T])
-        R = T * K
-        B.moe_permute(idx, self.expert_offset, self.E_local, self.workspace, self.expert_offsets,
-                      self.sorted_route[:R], self.route_row[:R])
+            B.moe_quant_mxfp8(x, xq, xs)
+            B.moe_permute(idx, self.expert_offset, self.E_local, self.workspace,
+                          self.expert_offsets, self.sorted_route[:R], self.route_row[:R])
         B.moe_fc1_situ(xq, xs, K, self.expert_offsets, self.sorted_route[:R], self.w13,
                        self.w13_s, self.workspace, self.alpha, self.beta, self.hq[:R],
                        self.hs[:R], tiled=self.tiled)

@@ -92,6 +92,33 @@ def test_permute_validation(lib):
     assert p(FAKE, 4, 2, 0, 8, FAKE, FAKE, FAKE, FAKE, 8, None) == 5          # ws too small
 
 
+def test_route_quant_permute_validation(lib):
+    f = lib.moe_route_quant_permute
+
+    def call(**kw):
+        a = dict(logits=FAKE, ld=8, bias=None, T=4, E=8, k=2, sc=1.0, x=FAKE, ld_x=128, H=128,
+                 off=0, el=8, idx=FAKE, w=FAKE, xq=FAKE, xs=FAKE, offs=FAKE, sr=FAKE, rr=FAKE,
+                 ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return f(a["logits"], a["ld"], a["bias"], a["T"], a["E"], a["k"], a["sc"], a["x"],
+                 a["ld_x"], a["H"], a["off"], a["el"], a["idx"], a["w"], a["xq"], a["xs"],
+                 a["offs"], a["sr"], a["rr"], a["ws"], a["wsb"], None)
+
+    assert call(k=0) == 2                 # top_k
+    assert call(k=9) == 2                 # top_k > E
+    assert call(ld=7) == 2                # ld_logits < E
+    assert call(H=100, ld_x=128) == 2     # H % 32
+    assert call(ld_x=64) == 2             # ld_x < H
+    assert call(off=-1) == 2              # expert offset
+    assert call(el=0) == 2                # E_local
+    assert call(x=None) == 1
+    assert call(offs=None) == 1
+    assert call(x=FAKE + 8) == 3          # x not 16-aligned
+    assert call(ld_x=132) == 3            # ld_x % 8
+    assert call(ws=FAKE + 16) == 3        # workspace alignment
+    assert call(wsb=8) == 5               # workspace too small
+
+
 def test_fc_validation(lib):
     f1 = lib.moe_fc1_situ
     args = [FAKE, FAKE, 4, 256, 128, 2, 4, FAKE, FAKE, FAKE, FAKE, 4.0, 25.0, FAKE, FAKE, FAKE,

@@ -196,6 +196,45 @@ def test_grouping_matches_oracle(T, K, E, E_local, offset):
     assert np.array_equal(to_np(rrow), r_rrow)
 
 
+@pytest.mark.parametrize("T,E,K,E_local,offset,H", [
+    (1, 896, 16, 896, 0, 7168),      # one decode token, the full expert set (one launch)
+    (8, 896, 16, 224, 448, 7168),    # decode batch, an EP window in the middle (one launch)
+    (16, 64, 8, 40, 10, 512),        # 16 tokens (one launch)
+    (16, 1000, 16, 1000, 0, 1024),   # LDS above 64 KB: three launches
+    (40, 256, 4, 100, 50, 256),      # T > 16: three launches
+    (5, 4, 2, 4, 0, 128),            # tiny
+])
+def test_route_quant_permute_matches_separate_calls(T, E, K, E_local, offset, H):
+    """moe_route_quant_permute gives the bytes of moe_route, moe_quant_mxfp8 and
+    moe_permute called one after the other (routing ids also against the
+    oracle)."""
+    m = _lib()
+    rng = np.random.default_rng(1000 + T * 7 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    x = synth.f32_to_bf16_bits((0.5 * rng.standard_normal((T, H))).astype(np.float32))
+    print(f"[front] T={T} E={E} K={K} E_local={E_local} offset={offset} H={H}", flush=True)
+    d_logits, d_bias = torch.from_numpy(logits).to(DEV), torch.from_numpy(bias).to(DEV)
+    d_x = torch.from_numpy(x.astype(np.int16)).to(DEV).view(torch.bfloat16)
+    nbytes = m.moe_workspace_size(T, K, E_local, 128, 128)
+    ws_a = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    ws_b = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+    idx_a, w_a = m.moe_route(d_logits, d_bias, K, 2.5)
+    xq_a, xs_a = m.moe_quant_mxfp8(d_x)
+    offs_a, sr_a, rr_a = m.moe_permute(idx_a, offset, E_local, ws_a)
+    got = m.moe_route_quant_permute(d_logits, d_bias, K, 2.5, d_x, offset, E_local, ws_b)
+    torch.cuda.synchronize()
+    idx_b, w_b, xq_b, xs_b, offs_b, sr_b, rr_b = got
+    for name, a, b in (("topk_idx", idx_a, idx_b), ("topk_w", w_a, w_b), ("xq", xq_a, xq_b),
+                       ("xs", xs_a, xs_b), ("expert_offsets", offs_a, offs_b),
+                       ("sorted_route", sr_a, sr_b), ("route_row", rr_a, rr_b)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+    n_prefix = 4 * 5 * (E_local + 1)        # the tile schedule at the workspace's start
+    assert torch.equal(ws_a[:n_prefix], ws_b[:n_prefix]), "tile prefix"
+    r_idx, _ = oracle.route(logits, bias, K, 2.5)
+    assert np.array_equal(to_np(idx_b), r_idx)
+
+
 def test_masked_slots_empty_experts_and_idle_tokens():
     cfg = synth.custom_config("mask", 300, T=40, H=256, I=128, E=12, K=4)
     act, w_np, w_dev = _small_case(cfg)
