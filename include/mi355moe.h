@@ -220,6 +220,26 @@ moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H,
 moe_status_t moe_prepack_w13(const uint8_t* w13, const uint8_t* w13_s, int E_local, int H, int I,
                              uint8_t* w13t, uint8_t* w13t_s, hipStream_t stream);
 
+/* Row order of a w13 tensor (fixed values).  Page 1 ("Real checkpoint
+ * contract") lists three: the Kimi-K3 checkpoint keeps [gate; up] halves
+ * (rows [0, I) gate, [I, 2I) up), the CUTLASS runner expects [up; gate]
+ * halves, and the GPT-OSS loader interleaves rows (row 2j gate j, row 2j+1 up
+ * j; page 3's de-interleave takes rows 0::2 as gate, 1::2 as up). */
+typedef enum moe_w13_layout {
+  MOE_W13_GATE_UP = 0,
+  MOE_W13_UP_GATE = 1,
+  MOE_W13_INTERLEAVED = 2
+} moe_w13_layout_t;
+
+/* moe_prepack_w13 for a w13 / w13_s whose rows are in `layout` order (a
+ * moe_w13_layout_t value; anything else is MOE_ERR_SHAPE).  The tiled result
+ * is the same bytes moe_prepack_w13 gives for the [gate; up] reordering of
+ * the input, so moe_fc1_situ_tiled computes the same layer for every layout.
+ * (The checkpoint-layout moe_fc1_situ reads [gate; up] only.) */
+moe_status_t moe_prepack_w13_layout(const uint8_t* w13, const uint8_t* w13_s, int E_local, int H,
+                                    int I, int layout, uint8_t* w13t, uint8_t* w13t_s,
+                                    hipStream_t stream);
+
 /* Reorder checkpoint w2 [E_local, H, I/2] + w2_s [E_local, H, I/32]. */
 moe_status_t moe_prepack_w2(const uint8_t* w2, const uint8_t* w2_s, int E_local, int H, int I,
                             uint8_t* w2t, uint8_t* w2t_s, hipStream_t stream);

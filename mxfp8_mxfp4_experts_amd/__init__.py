@@ -14,7 +14,11 @@ from ._binding import (  # noqa: F401
     moe_fc1_situ,
     moe_fc2_combine,
     moe_permute,
+    W13_GATE_UP,
+    W13_INTERLEAVED,
+    W13_UP_GATE,
     moe_prepack_w13,
+    moe_prepack_w13_layout,
     moe_prepack_w2,
     moe_quant_mxfp8,
     moe_route,

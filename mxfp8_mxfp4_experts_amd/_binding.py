@@ -27,7 +27,11 @@ EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_route", "moe_quant_mxfp8",
     "moe_permute", "moe_fc1_situ", "moe_fc2_combine", "moe_prepack_w13", "moe_prepack_w2",
     "moe_fc1_situ_tiled", "moe_fc2_combine_tiled", "moe_route_quant_permute",
+    "moe_prepack_w13_layout",
 )
+
+# moe_w13_layout_t values (row order of a w13 tensor)
+W13_GATE_UP, W13_UP_GATE, W13_INTERLEAVED = 0, 1, 2
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -70,6 +74,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     for name in ("moe_prepack_w13", "moe_prepack_w2"):
         getattr(lib, name).restype = _I
         getattr(lib, name).argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
+    lib.moe_prepack_w13_layout.restype = _I
+    lib.moe_prepack_w13_layout.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P]
     return lib
 
 
@@ -329,6 +335,19 @@ def moe_prepack_w13(w13, w13_s):
     """Checkpoint w13 [E, 2I, H/2] + scales -> tiled copies (same shapes)."""
     E, twoI, half_h = w13.shape
     return _prepack("moe_prepack_w13", w13, w13_s, 2 * half_h, twoI // 2)
+
+
+def moe_prepack_w13_layout(w13, w13_s, layout: int):
+    """w13 [E, 2I, H/2] + scales whose rows are in ``layout`` order
+    (W13_GATE_UP, W13_UP_GATE or W13_INTERLEAVED) -> tiled copies."""
+    _need(w13, "moe_prepack_w13_layout weights", torch.uint8)
+    _need(w13_s, "moe_prepack_w13_layout scales", torch.uint8, device=w13.device)
+    E, twoI, half_h = w13.shape
+    tw, tws = torch.empty_like(w13), torch.empty_like(w13_s)
+    _check("moe_prepack_w13_layout", lib().moe_prepack_w13_layout(
+        _ptr(w13), _ptr(w13_s), E, 2 * half_h, twoI // 2, int(layout), _ptr(tw), _ptr(tws),
+        _stream()))
+    return tw, tws
 
 
 def moe_prepack_w2(w2, w2_s):

@@ -280,8 +280,10 @@ moe_status_t moe_fc2_combine_tiled(const uint8_t* hq, const uint8_t* hs, int T, 
 }
 
 static moe_status_t prepack_impl(bool fc1, const uint8_t* w, const uint8_t* ws, int E_local,
-                                 int H, int I, uint8_t* tw, uint8_t* tws, hipStream_t stream) {
+                                 int H, int I, int layout, uint8_t* tw, uint8_t* tws,
+                                 hipStream_t stream) {
   if (!valid_hi(H, I) || E_local < 1 || E_local > kMaxExperts) return MOE_ERR_SHAPE;
+  if (layout < MOE_W13_GATE_UP || layout > MOE_W13_INTERLEAVED) return MOE_ERR_SHAPE;
   if (fc1 ? (I % 256 != 0) : (H % 512 != 0)) return MOE_ERR_SHAPE;
   if (!w || !ws || !tw || !tws) return MOE_ERR_NULL;
   if (!aligned(w, 16) || !aligned(ws, 16) || !aligned(tw, 16) || !aligned(tws, 16))
@@ -289,17 +291,23 @@ static moe_status_t prepack_impl(bool fc1, const uint8_t* w, const uint8_t* ws, 
   moe_status_t s = check_device();
   if (s != MOE_OK) return s;
   const int N = fc1 ? 2 * I : H, K = fc1 ? H : I;
-  return finish(launch_prepack(fc1, w, ws, E_local, N, K, I, tw, tws, stream));
+  return finish(launch_prepack(fc1, w, ws, E_local, N, K, I, layout, tw, tws, stream));
 }
 
 moe_status_t moe_prepack_w13(const uint8_t* w13, const uint8_t* w13_s, int E_local, int H, int I,
                              uint8_t* w13t, uint8_t* w13t_s, hipStream_t stream) {
-  return prepack_impl(true, w13, w13_s, E_local, H, I, w13t, w13t_s, stream);
+  return prepack_impl(true, w13, w13_s, E_local, H, I, MOE_W13_GATE_UP, w13t, w13t_s, stream);
+}
+
+moe_status_t moe_prepack_w13_layout(const uint8_t* w13, const uint8_t* w13_s, int E_local, int H,
+                                    int I, int layout, uint8_t* w13t, uint8_t* w13t_s,
+                                    hipStream_t stream) {
+  return prepack_impl(true, w13, w13_s, E_local, H, I, layout, w13t, w13t_s, stream);
 }
 
 moe_status_t moe_prepack_w2(const uint8_t* w2, const uint8_t* w2_s, int E_local, int H, int I,
                             uint8_t* w2t, uint8_t* w2t_s, hipStream_t stream) {
-  return prepack_impl(false, w2, w2_s, E_local, H, I, w2t, w2t_s, stream);
+  return prepack_impl(false, w2, w2_s, E_local, H, I, MOE_W13_GATE_UP, w2t, w2t_s, stream);
 }
 
 }  // extern "C"

@@ -40,9 +40,11 @@ struct FcParams;
 bool prefill_shape_ok(const FcParams& prm, bool fc1);
 hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* tile_prefix_all,
                              int n_cu, hipStream_t stream);
-// One-time reordering of checkpoint-layout weights into the tiled layout.
+// One-time reordering of checkpoint-layout weights into the tiled layout
+// (layout: w13 row order, 0 [gate; up], 1 [up; gate], 2 interleaved).
 hipError_t launch_prepack(bool fc1, const uint8_t* w, const uint8_t* ws, int E_local, int N,
-                          int K, int I, uint8_t* tw, uint8_t* tws, hipStream_t stream);
+                          int K, int I, int layout, uint8_t* tw, uint8_t* tws,
+                          hipStream_t stream);
 hipError_t launch_combine(const uint16_t* y, const int8_t* ye, int H, const int32_t* route_row,
                           const float* topk_w, int T, int K, uint16_t* out, int64_t ld_out,
                           hipStream_t stream);

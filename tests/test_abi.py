@@ -119,6 +119,15 @@ def test_route_quant_permute_validation(lib):
     assert call(wsb=8) == 5               # workspace too small
 
 
+def test_prepack_layout_validation(lib):
+    f = lib.moe_prepack_w13_layout
+    assert f(FAKE, FAKE, 2, 256, 256, 3, FAKE, FAKE, None) == 2       # unknown layout
+    assert f(FAKE, FAKE, 2, 256, 256, -1, FAKE, FAKE, None) == 2
+    assert f(FAKE, FAKE, 2, 256, 128, 2, FAKE, FAKE, None) == 2       # I % 256
+    assert f(None, FAKE, 2, 256, 256, 2, FAKE, FAKE, None) == 1
+    assert f(FAKE + 8, FAKE, 2, 256, 256, 1, FAKE, FAKE, None) == 3
+
+
 def test_fc_validation(lib):
     f1 = lib.moe_fc1_situ
     args = [FAKE, FAKE, 4, 256, 128, 2, 4, FAKE, FAKE, FAKE, FAKE, 4.0, 25.0, FAKE, FAKE, FAKE,

@@ -235,6 +235,34 @@ def test_route_quant_permute_matches_separate_calls(T, E, K, E_local, offset, H)
     assert np.array_equal(to_np(idx_b), r_idx)
 
 
+@pytest.mark.parametrize("layout", ["up_gate", "interleaved"])
+def test_prepack_w13_layouts(layout):
+    """w13 in [up; gate] halves or interleaved gate/up rows (page 1, real
+    checkpoint contract; page 3: gate = rows 0::2, up = rows 1::2) prepacks to
+    the bytes of the [gate; up] checkpoint."""
+    m = _lib()
+    cfg = synth.custom_config("layout", 307, T=1, H=512, I=256, E=3, K=1)
+    w = synth.make_expert_weights(cfg, device=torch.device(DEV))
+    I = cfg.I
+    print(f"[layout] {layout} E=3 H=512 I=256", flush=True)
+
+    def reorder(t):
+        gate, up = t[:, :I], t[:, I:]
+        if layout == "up_gate":
+            return torch.cat([up, gate], dim=1).contiguous()
+        out = torch.empty_like(t)
+        out[:, 0::2], out[:, 1::2] = gate, up
+        return out
+
+    code = m.W13_UP_GATE if layout == "up_gate" else m.W13_INTERLEAVED
+    ref_t, ref_s = m.moe_prepack_w13(w["w13"], w["w13_s"])
+    got_t, got_s = m.moe_prepack_w13_layout(reorder(w["w13"]), reorder(w["w13_s"]), code)
+    same_t, same_s = m.moe_prepack_w13_layout(w["w13"], w["w13_s"], m.W13_GATE_UP)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_t, got_t) and torch.equal(ref_s, got_s)
+    assert torch.equal(ref_t, same_t) and torch.equal(ref_s, same_s)
+
+
 def test_masked_slots_empty_experts_and_idle_tokens():
     cfg = synth.custom_config("mask", 300, T=40, H=256, I=128, E=12, K=4)
     act, w_np, w_dev = _small_case(cfg)
