@@ -203,9 +203,10 @@ static moe_status_t fc1_impl(const uint8_t* xq, const uint8_t* xs, int T, int H,
   char* ws = static_cast<char*>(workspace);
   const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + l.tile_prefix);
   uint32_t* act_st = reinterpret_cast<uint32_t*>(ws + l.act_st);
+  int32_t* sched = reinterpret_cast<int32_t*>(ws + l.fc_sched);
   return finish(launch_fc1(xq, xs, T, H, I, top_k, E_local, expert_offsets, sorted_route, w13,
-                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, act_st, n_cu, tiled,
-                           stream));
+                           w13_s, situ_alpha, situ_beta, hq, hs, prefix, act_st, sched, n_cu,
+                           tiled, stream));
 }
 
 moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
@@ -254,8 +255,9 @@ static moe_status_t fc2_impl(const uint8_t* hq, const uint8_t* hs, int T, int H,
   uint16_t* y = reinterpret_cast<uint16_t*>(ws + l.y);
   int8_t* ye = reinterpret_cast<int8_t*>(ws + l.ye);
   uint32_t* act_st = reinterpret_cast<uint32_t*>(ws + l.act_st);
+  int32_t* sched = reinterpret_cast<int32_t*>(ws + l.fc_sched);
   hipError_t e = launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, ye,
-                            prefix, act_st, n_cu, tiled, stream);
+                            prefix, act_st, sched, n_cu, tiled, stream);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return finish(launch_combine(y, ye, H, route_row, topk_w, T, top_k, out, ld_out, stream));
 }

@@ -25,6 +25,7 @@ constexpr int kNumTileSizes = 5;
 // ranking), 2048 above (few enough that the per-expert scan over chunks
 // stays short).
 constexpr int kPermSingle = 2048;
+constexpr int kSchedStride = 64;   // int32 stride between the per-XCD work counters
 __host__ __device__ inline int perm_chunk_size(int64_t R) { return R <= 16384 ? 256 : 2048; }
 inline int perm_chunks(int64_t R) {
   return R <= kPermSingle ? 0 : (int)((R + perm_chunk_size(R) - 1) / perm_chunk_size(R));
@@ -33,6 +34,7 @@ inline int perm_chunks(int64_t R) {
 struct WsLayout {
   size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1]
   size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
+  size_t fc_sched;      // int32 [8][kSchedStride]: per-XCD work counters of the prefill FC kernels
   size_t act_st;        // uint32 [max(H, I) / 128][T * top_k]: an FC input's scale dwords,
                         // stage-major in grouped-row order (prefill-shaped FC kernels)
   size_t y;             // fp16 [T * top_k][H]  (FC2 rows before the combine, scaled)
@@ -49,6 +51,8 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I) {
   off = align256(off + sizeof(int32_t) * kNumTileSizes * (size_t)(E_local + 1));
   l.perm_counts = off;
   off = align256(off + sizeof(int32_t) * (size_t)perm_chunks((int64_t)T * top_k) * E_local);
+  l.fc_sched = off;
+  off = align256(off + sizeof(int32_t) * 8 * kSchedStride);
   l.act_st = off;
   off = align256(off + (size_t)T * top_k * (size_t)((H > I ? H : I) / 32));
   l.y = off;

@@ -262,10 +262,11 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
                       uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all,
-                      uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream) {
+                      uint32_t* act_st, int32_t* sched, int n_cu, bool tiled,
+                      hipStream_t stream) {
   FcParams p{};
   p.act = xq; p.act_s = xs; p.act_rows = T; p.gather = sorted_route; p.top_k = top_k;
-  p.n_routes = (int64_t)T * top_k; p.act_st = act_st;
+  p.n_routes = (int64_t)T * top_k; p.act_st = act_st; p.sched = sched;
   p.w = w13; p.w_s = w13_s; p.K = H; p.N = 2 * I; p.I = I;
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = I / 32;
@@ -276,10 +277,11 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
                       uint16_t* y, int8_t* ye, const int32_t* tile_prefix_all,
-                      uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream) {
+                      uint32_t* act_st, int32_t* sched, int n_cu, bool tiled,
+                      hipStream_t stream) {
   FcParams p{};
   p.act = hq; p.act_s = hs; p.act_rows = (int64_t)T * top_k; p.gather = nullptr; p.top_k = top_k;
-  p.n_routes = (int64_t)T * top_k; p.act_st = act_st;
+  p.n_routes = (int64_t)T * top_k; p.act_st = act_st; p.sched = sched;
   p.w = w2; p.w_s = w2_s; p.K = I; p.N = H; p.I = I;
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = H / 64;

@@ -24,6 +24,7 @@ struct FcParams {
   int64_t act_rows;          // rows of act: FC1 T, FC2 R
   int64_t n_routes;          // grouped rows R = T * top_k
   uint32_t* act_st;          // workspace: [K/128][R] scale dwords of the grouped rows
+  int32_t* sched;            // workspace: per-XCD work counters (prefill kernels)
   const int32_t* gather;     // FC1: sorted_route (grouped row -> route); FC2: unused
   int top_k;
   const uint8_t* w;          // [E_local, N, K/2]

@@ -31,7 +31,8 @@
 //     eight bank groups;
 //   * an expert with at most 256 rows is one tile, so its weights are read
 //     once in total; its token rows are re-read by every column group, which
-//     the XCD-contiguous schedule keeps in that XCD's L2;
+//     the schedule keeps in one XCD's L2: each XCD owns a contiguous range of
+//     items and its workgroups take them in order from a shared counter;
 //   * per stage a wavefront reads its 8 weight operands once, then per valid
 //     token tile 8 MFMAs, each followed by a read of the next tile's operands
 //     or one of the stage's global loads.  The stage loop is instantiated per
@@ -67,7 +68,7 @@ constexpr int kTilePrefixIndex = 4;          // tile height 16 << 4 = 256
 constexpr int kMaxLdsExperts = 1024;            // local experts whose metadata LDS holds
 static_assert(kKS == kTileK && 2 * kBN == kTileRows, "tile shape");
 static_assert((16 << kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSizes, "tile prefix");
-constexpr int kLdsBytes = kNumBuf * kStage + 8 * (kMaxLdsExperts + 1);
+constexpr int kLdsBytes = kNumBuf * kStage + 8 * (kMaxLdsExperts + 1) + 16;
 static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
 // Loads issued per wavefront and stage: 4 token pieces, 2 weight pieces and
@@ -116,12 +117,16 @@ struct AOp {
 // bytes of MX blocks 4s .. 4s+3 of grouped row r's source row (FC1: token
 // gather[r] / top_k of act_s; FC2: row r).  The prefill kernels then load a
 // tile's scales for a stage as one contiguous run instead of one cache line
-// per row.  Only the kept rows [0, offs[E_local]) are written.
+// per row.  Only the kept rows [0, offs[E_local]) are written.  Also clears
+// the per-XCD work counters of the FC kernel that follows on the stream.
 __global__ __launch_bounds__(256) void stage_scales_kernel(const uint8_t* __restrict__ act_s,
                                                            int k32, const int32_t* __restrict__ gather,
                                                            int top_k, const int32_t* __restrict__ offs,
                                                            int E_local, int R, int n_stages,
-                                                           uint32_t* __restrict__ out) {
+                                                           uint32_t* __restrict__ out,
+                                                           int32_t* __restrict__ sched) {
+  // The FC kernel launched next takes its items from these counters.
+  if (blockIdx.x == 0 && threadIdx.x < 8) sched[threadIdx.x * kSchedStride] = 0;
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= offs[E_local]) return;
   const int src = gather ? gather[r] / top_k : r;
@@ -133,10 +138,11 @@ template <bool FC1, bool TILED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fc_prefill_kernel(FcParams p, int n_cg) {
   // One LDS object: the stage ring, then the expert tile prefix and row
-  // offsets (read once per workgroup).
+  // offsets (read once per workgroup), then the current item.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
   int* const prefix_s = reinterpret_cast<int*>(lds + kNumBuf * kStage);
   int* const offs_s = prefix_s + kMaxLdsExperts + 1;
+  int* const item_s = offs_s + kMaxLdsExperts + 1;
   lds_t* const lds_base = (lds_t*)lds;   // LDS address space: immediate offsets fold
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
@@ -150,9 +156,10 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
   }
   __syncthreads();
   const int n_items = prefix_s[p.E_local] * n_cg;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
   const int item_lo = (int)((int64_t)n_items * xcd / 8);
   const int item_hi = (int)((int64_t)n_items * (xcd + 1) / 8);
+  int32_t* const ctr = p.sched + xcd * kSchedStride;
   const __amdgpu_buffer_rsrc_t act_r = rsrc(p.act, (uint32_t)(p.act_rows * K));
 
   // LDS read offsets (lane parts; the tile's part goes into the immediate):
@@ -166,7 +173,15 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
   const int b_op = kWOff + 8192 * hw + 16 * (4 * li + (g ^ ((li >> 1) & 3)));
   const int b_sc = kWScaleOff + 512 * hw + 4 * li + g;
 
-  for (int item = item_lo + slot; item < item_hi; item += per_xcd) {
+  // The workgroups of one XCD take its items in order from a shared counter,
+  // so the items in flight are always a short run of neighbours (the column
+  // groups of one tile, reading the same token rows from L2) however long
+  // each item takes.
+  for (;;) {
+    if (tid == 0) item_s[0] = item_lo + atomicAdd(ctr, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(item_s[0]);
+    if (item >= item_hi || item < item_lo) break;
     const int e = __builtin_amdgcn_readfirstlane(find_expert_lds(prefix_s, p.E_local, item / n_cg));
     const int pe = __builtin_amdgcn_readfirstlane(prefix_s[e]);
     const int nt = __builtin_amdgcn_readfirstlane(prefix_s[e + 1]) - pe;
@@ -414,7 +429,8 @@ bool prefill_shape_ok(const FcParams& prm, bool fc1) {
   const int64_t K = prm.K;
   return K % kKS == 0 && (fc1 ? prm.I % 256 == 0 : prm.N % 512 == 0) && prm.E_local <= kMaxLdsExperts &&
          prm.act_rows * K < ((int64_t)1 << 31) && (int64_t)prm.N * (K / 2) < ((int64_t)1 << 31) &&
-         prm.n_routes * (K / 32) < ((int64_t)1 << 31) && prm.act_st != nullptr;
+         prm.n_routes * (K / 32) < ((int64_t)1 << 31) && prm.act_st != nullptr &&
+         prm.sched != nullptr;
 }
 
 hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* tile_prefix_all,
@@ -428,7 +444,7 @@ hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* 
   if (R > 0) {
     hipLaunchKernelGGL(stage_scales_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, prm.act_s,
                        prm.K / 32, fc1 ? prm.gather : nullptr, prm.top_k, prm.expert_offsets,
-                       prm.E_local, R, n_stages, prm.act_st);
+                       prm.E_local, R, n_stages, prm.act_st, prm.sched);
   }
   const dim3 grid(n_wg), block(kThreads);
   if (fc1 && tiled)

@@ -27,11 +27,13 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,
                       uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all,
-                      uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream);
+                      uint32_t* act_st, int32_t* sched, int n_cu, bool tiled,
+                      hipStream_t stream);
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
                       uint16_t* y, int8_t* ye, const int32_t* tile_prefix_all,
-                      uint32_t* act_st, int n_cu, bool tiled, hipStream_t stream);
+                      uint32_t* act_st, int32_t* sched, int n_cu, bool tiled,
+                      hipStream_t stream);
 struct FcParams;
 // Prefill-shaped FC kernels (fc_prefill.hip): usable when K % 128 == 0, the
 // weight rows split into whole 512-row groups and the operands fit 32-bit
