@@ -34,7 +34,8 @@ inline int perm_chunks(int64_t R) {
 struct WsLayout {
   size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1]
   size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
-  size_t fc_sched;      // int32 [8][kSchedStride]: per-XCD work counters of the prefill FC kernels
+  size_t fc_sched;      // int32 [9][kSchedStride]: per-XCD work counters of the prefill FC
+                        // kernels, then their 9 item-range bounds
   size_t act_st;        // uint32 [max(H, I) / 128][T * top_k]: an FC input's scale dwords,
                         // stage-major in grouped-row order (prefill-shaped FC kernels)
   size_t y;             // fp16 [T * top_k][H]  (FC2 rows before the combine, scaled)
@@ -52,7 +53,7 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I) {
   l.perm_counts = off;
   off = align256(off + sizeof(int32_t) * (size_t)perm_chunks((int64_t)T * top_k) * E_local);
   l.fc_sched = off;
-  off = align256(off + sizeof(int32_t) * 8 * kSchedStride);
+  off = align256(off + sizeof(int32_t) * 9 * kSchedStride);
   l.act_st = off;
   off = align256(off + (size_t)T * top_k * (size_t)((H > I ? H : I) / 32));
   l.y = off;

@@ -32,7 +32,8 @@
 //   * an expert with at most 256 rows is one tile, so its weights are read
 //     once in total; its token rows are re-read by every column group, which
 //     the schedule keeps in one XCD's L2: each XCD owns a contiguous range of
-//     items and its workgroups take them in order from a shared counter;
+//     items (split by estimated work) and its workgroups take them in order
+//     from a shared counter;
 //   * per stage a wavefront reads its 8 weight operands once, then per valid
 //     token tile 8 MFMAs, each followed by a read of the next tile's operands
 //     or one of the stage's global loads.  The stage loop is instantiated per
@@ -118,15 +119,80 @@ struct AOp {
 // gather[r] / top_k of act_s; FC2: row r).  The prefill kernels then load a
 // tile's scales for a stage as one contiguous run instead of one cache line
 // per row.  Only the kept rows [0, offs[E_local]) are written.  Also clears
-// the per-XCD work counters of the FC kernel that follows on the stream.
+// the per-XCD work counters of the FC kernel that follows on the stream and
+// writes its per-XCD item ranges.
+// Items of one FC launch, split over the 8 XCDs by estimated work: an item
+// (expert e, column group, 256-row tile) costs about kItemFixedRows + its rows
+// rounded up to 16 per stage.  Workgroup 0 of the pre-pass scans the
+// per-expert work (n_cg column groups of its tiles) and writes the first item
+// of each XCD's range (at a column-group boundary) to bounds[0..8].
+constexpr int kItemFixedRows = 64;
+
+__device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __restrict__ prefix,
+                            int E_local, int n_cg, int32_t* __restrict__ bounds) {
+  __shared__ long long cum_s[kMaxLdsExperts + 1];
+  __shared__ long long part_s[256];
+  const int tid = threadIdx.x;
+  const int per = (E_local + 255) / 256, e0 = tid * per;
+  long long mine = 0;
+  for (int e = e0; e < e0 + per && e < E_local; ++e) {
+    const int c = offs[e + 1] - offs[e], nt = prefix[e + 1] - prefix[e];
+    const long long w = (long long)n_cg * (nt * kItemFixedRows + 16 * ((c + 15) / 16));
+    cum_s[e + 1] = w;   // turned into a running sum below
+    mine += w;
+  }
+  part_s[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    long long run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const long long v = part_s[i];
+      part_s[i] = run;
+      run += v;
+    }
+    cum_s[0] = 0;
+  }
+  __syncthreads();
+  long long run = part_s[tid];
+  for (int e = e0; e < e0 + per && e < E_local; ++e) {
+    run += cum_s[e + 1];
+    cum_s[e + 1] = run;
+  }
+  __syncthreads();
+  if (tid <= 8) {
+    const long long total = cum_s[E_local];
+    const int n_items = prefix[E_local] * n_cg;
+    int item = tid == 8 ? n_items : 0;
+    if (tid > 0 && tid < 8 && total > 0) {
+      const long long target = total * tid / 8;
+      int lo = 0, hi = E_local;   // largest e with cum[e] <= target
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cum_s[mid] <= target) lo = mid; else hi = mid;
+      }
+      const int e = lo, nt = prefix[e + 1] - prefix[e];
+      const long long per_cg = nt > 0 ? (cum_s[e + 1] - cum_s[e]) / n_cg : 1;
+      long long cg = per_cg > 0 ? (target - cum_s[e]) / per_cg : 0;
+      cg = cg < n_cg ? cg : n_cg;
+      item = prefix[e] * n_cg + (int)cg * nt;
+    }
+    bounds[tid] = item;
+  }
+}
+
 __global__ __launch_bounds__(256) void stage_scales_kernel(const uint8_t* __restrict__ act_s,
                                                            int k32, const int32_t* __restrict__ gather,
                                                            int top_k, const int32_t* __restrict__ offs,
-                                                           int E_local, int R, int n_stages,
-                                                           uint32_t* __restrict__ out,
+                                                           const int32_t* __restrict__ prefix,
+                                                           int E_local, int n_cg, int R,
+                                                           int n_stages, uint32_t* __restrict__ out,
                                                            int32_t* __restrict__ sched) {
-  // The FC kernel launched next takes its items from these counters.
-  if (blockIdx.x == 0 && threadIdx.x < 8) sched[threadIdx.x * kSchedStride] = 0;
+  // The FC kernel launched next takes its items from these counters and
+  // ranges.
+  if (blockIdx.x == 0) {
+    if (threadIdx.x < 8) sched[threadIdx.x * kSchedStride] = 0;
+    split_items(offs, prefix, E_local, n_cg, sched + 8 * kSchedStride);
+  }
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= offs[E_local]) return;
   const int src = gather ? gather[r] / top_k : r;
@@ -155,10 +221,9 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     offs_s[i] = p.expert_offsets[i];
   }
   __syncthreads();
-  const int n_items = prefix_s[p.E_local] * n_cg;
   const int xcd = blockIdx.x & 7;
-  const int item_lo = (int)((int64_t)n_items * xcd / 8);
-  const int item_hi = (int)((int64_t)n_items * (xcd + 1) / 8);
+  const int item_lo = p.sched[8 * kSchedStride + xcd];
+  const int item_hi = p.sched[8 * kSchedStride + xcd + 1];
   int32_t* const ctr = p.sched + xcd * kSchedStride;
   const __amdgpu_buffer_rsrc_t act_r = rsrc(p.act, (uint32_t)(p.act_rows * K));
 
@@ -444,7 +509,7 @@ hipError_t launch_fc_prefill(bool fc1, bool tiled, FcParams prm, const int32_t* 
   if (R > 0) {
     hipLaunchKernelGGL(stage_scales_kernel, dim3((R + 255) / 256), dim3(256), 0, stream, prm.act_s,
                        prm.K / 32, fc1 ? prm.gather : nullptr, prm.top_k, prm.expert_offsets,
-                       prm.E_local, R, n_stages, prm.act_st, prm.sched);
+                       prm.tile_prefix, prm.E_local, n_cg, R, n_stages, prm.act_st, prm.sched);
   }
   const dim3 grid(n_wg), block(kThreads);
   if (fc1 && tiled)
