@@ -111,6 +111,8 @@ MID_SHAPES = [
     dict(T=700, H=768, I=256, E=32, K=4, E_local=8, expert_offset=16),
     # more than one grouping chunk (2048 routes) and ~600 rows per expert
     dict(T=1200, H=512, I=256, E=6, K=3),
+    # the largest top_k (64): every token routed to every expert
+    dict(T=40, H=256, I=256, E=64, K=64),
 ]
 
 
@@ -328,6 +330,34 @@ def test_route_strided_logits_and_full_width():
     assert np.array_equal(to_np(ids), rid)
     ulp = np.abs(to_np(w).view(np.int32).astype(np.int64) - rw.view(np.int32).astype(np.int64))
     assert ulp.max() <= 4
+
+
+@pytest.mark.parametrize("T,E,K", [
+    (5, 4096, 64),     # the largest routing width and top_k (LDS path)
+    (7, 1500, 16),     # past the register path
+    (4, 1024, 64),     # the register path at its widest, largest top_k
+    (3, 64, 64),       # top_k = E: every expert selected
+    (9, 1025, 3),
+])
+def test_route_limits(T, E, K):
+    """Routing at the size limits of the C ABI (E up to 4096, top_k up to 64,
+    top_k = E) against the oracle; also through the fused front call."""
+    m = _lib()
+    rng = np.random.default_rng(500 + E + K)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(E)).astype(np.float32)
+    print(f"[route limits] T={T} E={E} K={K}", flush=True)
+    d_lg, d_b = torch.from_numpy(logits).to(DEV), torch.from_numpy(bias).to(DEV)
+    ids, w = m.moe_route(d_lg, d_b, K, 1.0)
+    rid, rw = oracle.route(logits, bias, K, 1.0)
+    assert np.array_equal(to_np(ids), rid)
+    ulp = np.abs(to_np(w).view(np.int32).astype(np.int64) - rw.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 4
+    x = torch.zeros((T, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(m.moe_workspace_size(T, K, E, 128, 128), dtype=torch.uint8, device=DEV)
+    f_ids, f_w = m.moe_route_quant_permute(d_lg, d_b, K, 1.0, x, 0, E, ws)[:2]
+    torch.cuda.synchronize()
+    assert torch.equal(f_ids, ids) and torch.equal(f_w.view(torch.int32), w.view(torch.int32))
 
 
 def test_quant_exhaustive_bf16_patterns():
