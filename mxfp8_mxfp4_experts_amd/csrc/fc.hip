@@ -35,15 +35,22 @@ namespace mi355moe {
 
 namespace {
 
-// Operands of one 512-K super-step for one wavefront.
+// 128-K slices per super-step: the operands of two super-steps are in
+// registers at a time (about 120 VGPRs for two slices), which leaves room for
+// two wavefronts per SIMD.
+#ifndef DECODE_SJ
+#define DECODE_SJ 2
+#endif
+constexpr int kSJ = DECODE_SJ;
+
+// Operands of one super-step (kSJ 128-K slices) for one wavefront.
 template <int NT>
 struct Stage {
-  v4i w[4][4];      // [row block][MFMA j]: 32 E2M1 weights of this lane
-  v4i ws[4];        // [row block]: the row's 16 scale bytes of the super-step
-                    // (dword j = MX blocks 16S + 4j .. 16S + 4j + 3)
-  v4i alo[NT][4];   // [token tile][MFMA j]: E4M3 K [16g, 16g+16) of the slice
-  v4i ahi[NT][4];   //                      E4M3 K [64+16g, 64+16g+16)
-  v4i as[NT];       // the token's 16 scale bytes
+  v4i w[4][kSJ];      // [row block][MFMA j]: 32 E2M1 weights of this lane
+  int ws[4][kSJ];     // [row block][MFMA j]: the row's 4 scale bytes of slice j
+  v4i alo[NT][kSJ];   // [token tile][MFMA j]: E4M3 K [16g, 16g+16) of the slice
+  v4i ahi[NT][kSJ];   //                      E4M3 K [64+16g, 64+16g+16)
+  int as[NT][kSJ];    // the token's 4 scale bytes of slice j
 };
 
 // Checkpoint layout: wp[bk] points at the lane's row + 16g, wsp[bk] at the
@@ -58,27 +65,30 @@ __device__ __forceinline__ void load_stage(Stage<NT>& st, const uint8_t* const* 
   for (int bk = 0; bk < 4; ++bk) {
     if (TILED) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kSJ; ++j) {
         st.w[bk][j] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4i*>(wp[bk] + (size_t)(4 * S + j) * kTileBytes));
-        st.ws[bk][j] = *reinterpret_cast<const int*>(wsp[bk] + (size_t)(4 * S + j) * kTileScaleBytes);
+            reinterpret_cast<const v4i*>(wp[bk] + (size_t)(kSJ * S + j) * kTileBytes));
+        st.ws[bk][j] =
+            *reinterpret_cast<const int*>(wsp[bk] + (size_t)(kSJ * S + j) * kTileScaleBytes);
       }
     } else {
-      const v4i* src = reinterpret_cast<const v4i*>(wp[bk] + (size_t)S * 256);
+      const v4i* src = reinterpret_cast<const v4i*>(wp[bk] + (size_t)S * 64 * kSJ);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st.w[bk][j] = __builtin_nontemporal_load(src + 4 * j);
-      st.ws[bk] = *reinterpret_cast<const v4i*>(wsp[bk] + (size_t)S * 16);
+      for (int j = 0; j < kSJ; ++j) {
+        st.w[bk][j] = __builtin_nontemporal_load(src + 4 * j);
+        st.ws[bk][j] = *reinterpret_cast<const int*>(wsp[bk] + (size_t)(kSJ * S + j) * 4);
+      }
     }
   }
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
-    const uint8_t* a = ap[tt] + (size_t)S * 512 + 16 * g;
+    const uint8_t* a = ap[tt] + (size_t)S * 128 * kSJ + 16 * g;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kSJ; ++j) {
       st.alo[tt][j] = *reinterpret_cast<const v4i*>(a + 128 * j);
       st.ahi[tt][j] = *reinterpret_cast<const v4i*>(a + 128 * j + 64);
+      st.as[tt][j] = *reinterpret_cast<const int*>(asp[tt] + (size_t)(kSJ * S + j) * 4);
     }
-    st.as[tt] = *reinterpret_cast<const v4i*>(asp[tt] + (size_t)S * 16);
   }
 }
 
@@ -88,7 +98,7 @@ __device__ __forceinline__ void compute_stage(v4f (&acc)[NT][4], const Stage<NT>
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kSJ; ++j) {
       const int asv = st.as[tt][j] >> sh;
 #pragma unroll
       for (int bk = 0; bk < 4; ++bk)
@@ -164,13 +174,13 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk) acc[tt][bk] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Super-steps of 512 K: MFMA j takes the 128-K slice [512S + 128j, +128) in
-  // natural order, so slot b holds MX block 16S + 4j + b.  Both operands'
-  // scales for the super-step are one 16-byte chunk per row; lane group g
-  // uses byte 4j + g of it (a shift by 8g of dword j).  The next super-step's
+  // Super-steps of 128 kSJ K: MFMA j takes the 128-K slice
+  // [128 (kSJ S + j), +128) in natural order, so slot b holds MX block
+  // 4 (kSJ S + j) + b.  Both operands' scales for slice j are one dword per
+  // row; lane group g uses byte g of it (a shift by 8g).  The next super-step's
   // operands are loaded before this one's MFMAs are issued (two register
   // stages), keeping a wavefront's weight stream in flight.
-  const int n_super = K / 512;
+  const int n_super = K / (128 * kSJ);
   Stage<NT> st0, st1;
   // No branch inside the loop: the wait-count pass then lets the stage just
   // loaded stay in flight while the other stage's MFMAs issue.  When n_super
@@ -189,7 +199,7 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   }
   if (S < n_super) compute_stage<NT>(acc, st0, g);
   // Remaining 128-K steps (K not a multiple of 512): slot b takes block 4s + b.
-  for (int s = n_super * 4; s < K / 128; ++s) {
+  for (int s = n_super * kSJ; s < K / 128; ++s) {
     v4i wv[4];
     int wsv[4];
 #pragma unroll
