@@ -56,8 +56,17 @@ struct Stage {
 // Checkpoint layout: wp[bk] points at the lane's row + 16g, wsp[bk] at the
 // row's scale bytes.  Tiled layout: wp[bk] points at the lane's 16 bytes in
 // stage 0's block and wsp[bk] at the row's scale dword there; stage t adds t
-// whole blocks.
-template <int NT, bool TILED>
+// whole blocks.  STREAM: the weights are read once (the expert has a single
+// tile), so they are loaded non-temporally and do not displace lines that
+// other tiles will reuse; otherwise they stay cached for the expert's next
+// tile.
+template <bool STREAM>
+__device__ __forceinline__ v4i load_weights(const v4i* p) {
+  if (STREAM) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <int NT, bool TILED, bool STREAM>
 __device__ __forceinline__ void load_stage(Stage<NT>& st, const uint8_t* const* wp,
                                            const uint8_t* const* wsp, const uint8_t* const* ap,
                                            const uint8_t* const* asp, int S, int g) {
@@ -66,7 +75,7 @@ __device__ __forceinline__ void load_stage(Stage<NT>& st, const uint8_t* const* 
     if (TILED) {
 #pragma unroll
       for (int j = 0; j < kSJ; ++j) {
-        st.w[bk][j] = __builtin_nontemporal_load(
+        st.w[bk][j] = load_weights<STREAM>(
             reinterpret_cast<const v4i*>(wp[bk] + (size_t)(kSJ * S + j) * kTileBytes));
         st.ws[bk][j] =
             *reinterpret_cast<const int*>(wsp[bk] + (size_t)(kSJ * S + j) * kTileScaleBytes);
@@ -75,7 +84,7 @@ __device__ __forceinline__ void load_stage(Stage<NT>& st, const uint8_t* const* 
       const v4i* src = reinterpret_cast<const v4i*>(wp[bk] + (size_t)S * 64 * kSJ);
 #pragma unroll
       for (int j = 0; j < kSJ; ++j) {
-        st.w[bk][j] = __builtin_nontemporal_load(src + 4 * j);
+        st.w[bk][j] = load_weights<STREAM>(src + 4 * j);
         st.ws[bk][j] = *reinterpret_cast<const int*>(wsp[bk] + (size_t)(kSJ * S + j) * 4);
       }
     }
@@ -108,8 +117,37 @@ __device__ __forceinline__ void compute_stage(v4f (&acc)[NT][4], const Stage<NT>
   }
 }
 
+// The super-step loop over K / (128 kSJ) steps.  No branch inside the loop:
+// the wait-count pass then lets the stage just loaded stay in flight while the
+// other stage's MFMAs issue.  When n_super is even the last iteration reloads
+// the final stage.
+template <int NT, bool TILED, bool STREAM>
+__device__ __forceinline__ void super_steps(v4f (&acc)[NT][4], const uint8_t* const* wp,
+                                            const uint8_t* const* wsp, const uint8_t* const* ap,
+                                            const uint8_t* const* asp, int n_super, int g) {
+  Stage<NT> st0, st1;
+  if (n_super > 0) load_stage<NT, TILED, STREAM>(st0, wp, wsp, ap, asp, 0, g);
+  int S = 0;
+  for (; S + 1 < n_super; S += 2) {
+    load_stage<NT, TILED, STREAM>(st1, wp, wsp, ap, asp, S + 1, g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<NT>(acc, st0, g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage<NT, TILED, STREAM>(st0, wp, wsp, ap, asp, min(S + 2, n_super - 1), g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<NT>(acc, st1, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (S < n_super) compute_stage<NT>(acc, st0, g);
+}
+
+// Two-tile workgroups are held to two wavefronts per SIMD (a weight stream
+// in flight while the other wavefront's MFMAs issue).  One-tile workgroups
+// are left at the compiler's choice: two wavefronts at 176 VGPRs measured
+// faster than three at 168.
 template <bool FC1, int NT, bool TILED>
-__global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 1 : 2))) void
+fc_kernel(FcParams p) {
   // Consecutive block ids land on different XCDs (round robin over 8); remap
   // so that each XCD walks a contiguous range of (column group, tile) items,
   // with the tiles of one expert adjacent and sharing its weights in L2.
@@ -179,26 +217,16 @@ __global__ __launch_bounds__(256) void fc_kernel(FcParams p) {
   // 4 (kSJ S + j) + b.  Both operands' scales for slice j are one dword per
   // row; lane group g uses byte g of it (a shift by 8g).  The next super-step's
   // operands are loaded before this one's MFMAs are issued (two register
-  // stages), keeping a wavefront's weight stream in flight.
+  // stages), keeping a wavefront's weight stream in flight.  The weights of an
+  // expert with one tile are streamed past the caches; an expert with several
+  // tiles (whose workgroups run at about the same time on one XCD) keeps them
+  // in L2 for its other tiles.
   const int n_super = K / (128 * kSJ);
-  Stage<NT> st0, st1;
-  // No branch inside the loop: the wait-count pass then lets the stage just
-  // loaded stay in flight while the other stage's MFMAs issue.  When n_super
-  // is even the last iteration reloads the final stage (an L2 hit).
-  if (n_super > 0) load_stage<NT, TILED>(st0, wp, wsp, ap, asp, 0, g);
-  int S = 0;
-  for (; S + 1 < n_super; S += 2) {
-    load_stage<NT, TILED>(st1, wp, wsp, ap, asp, S + 1, g);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_stage<NT>(acc, st0, g);
-    __builtin_amdgcn_sched_barrier(0);
-    load_stage<NT, TILED>(st0, wp, wsp, ap, asp, min(S + 2, n_super - 1), g);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_stage<NT>(acc, st1, g);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (S < n_super) compute_stage<NT>(acc, st0, g);
-  // Remaining 128-K steps (K not a multiple of 512): slot b takes block 4s + b.
+  if (prefix[e + 1] - prefix[e] == 1)
+    super_steps<NT, TILED, true>(acc, wp, wsp, ap, asp, n_super, g);
+  else
+    super_steps<NT, TILED, false>(acc, wp, wsp, ap, asp, n_super, g);
+  // Remaining 128-K steps (K not a multiple of 128 kSJ): slot b takes block 4s + b.
   for (int s = n_super * kSJ; s < K / 128; ++s) {
     v4i wv[4];
     int wsv[4];
