@@ -12,15 +12,18 @@
 //     token quarter w >> 1 (the 16-row tiles q, q+4, q+8, q+12, so a partly
 //     filled tile still spreads over all four SIMDs): 4 tiles x 8 row blocks
 //     of 16x16 accumulators, 128 AGPRs;
-//   * both operands go through a ring of 3 LDS stages of 50 KB (256 token
-//     rows x 128 bytes, 256 token scale dwords, 256 weight rows x 64 bytes,
-//     256 weight scale dwords), filled by direct buffer -> LDS loads two
-//     stages ahead: every wavefront issues 7 per stage (4 KB of token rows,
-//     2 KB of weights, and the token or the weight scale dwords), so one
-//     fixed "s_waitcnt vmcnt(7)" per stage leaves exactly the next stage in
-//     flight; past the last stage the final stage is reloaded to keep that
-//     count.  The loads sit in the odd MFMA slots of the first two tiles
-//     (early in the stage: the longest lead before their wait);
+//   * both operands go through a ring of LDS stages (token rows x 128 bytes,
+//     token scale dwords, 256 weight rows x 64 bytes, weight scale dwords),
+//     filled by direct buffer -> LDS loads issued ahead: an item with up to
+//     256 rows in use has 3 stages of 50 KB and loads 2 ahead; one with up to
+//     128 or 64 rows has 4 stages of 34 KB or 5 of 26 KB and loads 3 or 4
+//     ahead, since its time is the latency of its weight stream.  Every
+//     wavefront issues the same loads per stage (token rows, 2 KB of weights,
+//     and the token or the weight scale dwords), so one fixed
+//     "s_waitcnt vmcnt" per stage leaves exactly the later stages in flight;
+//     past the last stage the final stage is reloaded to keep that count.
+//     The loads sit in MFMA slots early in the stage (the longest lead before
+//     their wait);
 //   * the token scale dwords are first restaged (stage_scales_kernel) into a
 //     stage-major array in grouped-row order, so a tile's scales for one stage
 //     are one contiguous 1 KB run instead of one cache line per row: the
@@ -60,22 +63,36 @@ constexpr int kBM = 256;                     // token rows per tile
 constexpr int kBN = 256;                     // weight rows per tile (4 units)
 constexpr int kKS = 128;                     // K per stage
 constexpr int kThreads = 512;                // 8 wavefronts
-constexpr int kTokScaleOff = kBM * kKS;      // 32768: token scale dwords
-constexpr int kWOff = kTokScaleOff + kBM * 4;        // 33792: weight operands
-constexpr int kWScaleOff = kWOff + kBN * kKS / 2;    // 50176: weight scale dwords
-constexpr int kStage = kWScaleOff + kBN * 4;         // 51200
-constexpr int kNumBuf = 3;                   // LDS ring depth
 constexpr int kTilePrefixIndex = 4;          // tile height 16 << 4 = 256
 constexpr int kMaxLdsExperts = 1024;            // local experts whose metadata LDS holds
 static_assert(kKS == kTileK && 2 * kBN == kTileRows, "tile shape");
 static_assert((16 << kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSizes, "tile prefix");
-constexpr int kLdsBytes = kNumBuf * kStage + 8 * (kMaxLdsExperts + 1) + 16;
-static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
-// Loads issued per wavefront and stage: 4 token pieces, 2 weight pieces and
-// 1 scale piece, all direct to LDS.  When stage s + 1 is waited for, only
-// stage s + 2's 7 remain in flight.
-constexpr int kLoadsPerStage = 7;
+// Stage layout of the LDS ring for an item whose used token rows fit in
+// 64 P (P = 4, 2 or 1 one-KB token pieces per wavefront and stage):
+// [token rows 8P KB][token scale dwords 1 KB][weight operands 16 KB][weight
+// scale dwords 1 KB].  A smaller token part leaves room for more stages, so
+// an item with few rows, whose time is its weight stream's latency, loads
+// further ahead: 2, 3 or 4 stages for P = 4, 2, 1.  Each wavefront issues
+// P + 3 direct-to-LDS loads per stage (P token pieces, 2 weight pieces, the
+// token or the weight scale dwords); when stage s + 1 is waited for, the
+// loads of the kAhead - 1 stages after it stay in flight.
+template <int P>
+struct Ring {
+  static constexpr int kTokScaleOff = 64 * P * kKS;
+  static constexpr int kWOff = kTokScaleOff + kBM * 4;
+  static constexpr int kWScaleOff = kWOff + kBN * kKS / 2;
+  static constexpr int kStage = kWScaleOff + kBN * 4;
+  static constexpr int kNumBuf = P == 4 ? 3 : P == 2 ? 4 : 5;
+  static constexpr int kAhead = kNumBuf - 1;
+  static constexpr int kLoads = P + 3;
+  static constexpr int kBytes = kNumBuf * kStage;
+};
+constexpr int kRingBytes = Ring<4>::kBytes;   // 153600, the largest of the three
+static_assert(Ring<2>::kBytes <= kRingBytes && Ring<1>::kBytes <= kRingBytes, "ring");
+static_assert((Ring<1>::kAhead - 1) * Ring<1>::kLoads < 64, "vmcnt");
+constexpr int kLdsBytes = kRingBytes + 8 * (kMaxLdsExperts + 1) + 16;
+static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
 // Raw buffer resource: base and byte size in SGPRs.  Sizes stay below 2^31,
 // so kOutOfRange (plus any stage offset) is always past the end.
@@ -201,16 +218,238 @@ __global__ __launch_bounds__(256) void stage_scales_kernel(const uint8_t* __rest
   for (int s = 0; s < n_stages; ++s) out[(size_t)s * R + r] = row[s];
 }
 
+// Per-lane constants of a workgroup: wavefront, lane, weight half, token
+// quarter, lane group and row, and the LDS read offsets within a stage.
+struct LaneGeom {
+  int wave, lane, hw, qt, g, li;
+  int a_lo, a_hi, a_sc, b_op, b_sc;
+};
+
+// One item: column group, first grouped row, valid rows, this wavefront's
+// token tiles, rows in use (whole 16-row tiles), stages and K.
+struct ItemGeom {
+  int cg, row_begin, n_valid, nj, rows_used, n_stages, K;
+};
+
+// One item with stage layout Ring<P> (rows_used <= 64 P): token row
+// offsets, the stage loop and the epilogue.  act_r / w_r / s_r are the
+// token-row, weight and scale buffers with this lane's offsets w_voff and
+// s_voff, advanced by w_step / s_step bytes per stage.
+template <bool FC1, bool TILED, int P>
+__device__ __forceinline__ void prefill_item(const FcParams& p, uint8_t* lds, const LaneGeom& lg,
+                                             const ItemGeom& it, __amdgpu_buffer_rsrc_t act_r,
+                                             __amdgpu_buffer_rsrc_t w_r, __amdgpu_buffer_rsrc_t s_r,
+                                             const uint32_t (&w_voff)[2], uint32_t s_voff,
+                                             int w_step, int s_step) {
+  using RG = Ring<P>;
+  lds_t* const lds_base = (lds_t*)lds;
+  const int wave = lg.wave, lane = lg.lane, hw = lg.hw, qt = lg.qt, g = lg.g, li = lg.li;
+  const int a_lo = lg.a_lo, a_hi = lg.a_hi, a_sc = lg.a_sc, b_op = lg.b_op, b_sc = lg.b_sc;
+  const int cg = it.cg, row_begin = it.row_begin, n_valid = it.n_valid, nj = it.nj;
+  const int rows_used = it.rows_used, n_stages = it.n_stages, K = it.K;
+  // LDS place of this wavefront's scale dwords.
+  const int s_lds =
+      wave < 4 ? RG::kTokScaleOff + 256 * wave : RG::kWScaleOff + 256 * (wave - 4);
+  // Token rows: wavefront w fills rows 8 (P w + i) + l / 8 (i < P);
+  // physical chunk l % 8 of a row takes logical chunk (l % 8) ^ (row & 7).
+  // Source rows are all read before any is used, so the gather latencies
+  // overlap; rows past the expert's last repeat that row.  Rows of unused
+  // tiles get an offset past the buffer's end, which the buffer unit
+  // answers with zeros without touching memory (so every wavefront still
+  // issues the same loads).
+  int src[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int tok = 8 * (P * wave + i) + (lane >> 3);
+    const int row = row_begin + min(tok, n_valid - 1);
+    src[i] = FC1 ? p.gather[row] : row;
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    asm volatile("" : "+v"(src[i]));
+    if (FC1) src[i] /= p.top_k;
+  }
+  uint32_t a_voff[P];
+  const int ac = (lane & 7) ^ ((lane >> 3) & 7);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int tok = 8 * (P * wave + i) + (lane >> 3);
+    a_voff[i] = tok < rows_used ? (uint32_t)src[i] * K + 16 * ac : kOutOfRange;
+  }
+
+  // Load q of stage s_load into stage buffer s_load % kNumBuf: q < P a 1 KB
+  // piece of token rows, q = P, P + 1 a weight piece, q = P + 2 the scale
+  // dwords.
+  auto issue_load = [&](int q, int s_load) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(s_load));
+    const int sc = min(s_load, n_stages - 1);
+    uint8_t* base = lds + (s_load % RG::kNumBuf) * RG::kStage;
+    if (q < P)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + 1024 * (P * wave + q), 16,
+                                               a_voff[q], kKS * sc, 0, 0);
+    else if (q < P + 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_r, base + RG::kWOff + 1024 * (2 * wave + q - P),
+                                               16, w_voff[q - P], w_step * sc, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_r, base + s_lds, 4, s_voff, s_step * sc, 0, 0);
+  };
+
+  // Stage buffer of stage s.  The offset is made opaque so that the compiler
+  // cannot prove later tiles' reads in bounds and hoist them.
+  auto stage_buf = [&](int s) __attribute__((always_inline)) {
+    int off = (s % RG::kNumBuf) * RG::kStage;
+    asm volatile("" : "+s"(off));
+    return static_cast<const lds_t*>(lds_base) + off;
+  };
+
+  // The stage loop for a wavefront holding NJ valid token tiles (a
+  // compile-time count, so no accumulator is conditionally updated).
+  auto run = [&](auto nji) __attribute__((always_inline)) {
+    constexpr int NJ = decltype(nji)::value;
+    v4f acc[NJ > 0 ? NJ : 1][2][4];  // [token tile j][unit k][row block i]
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[j][k][i] = v4f{0.f, 0.f, 0.f, 0.f};
+          asm volatile("" : "+a"(acc[j][k][i]));   // distinct registers from the start
+        }
+    AOp abuf[2];
+    v4i bw[2][4];   // weight operands of the stage: [unit k][row block i]
+    int bs[2][4];
+
+    // Operands of stage s's start: tile 0 and the weights.
+    auto read_start = [&](int s) __attribute__((always_inline)) {
+      if constexpr (NJ > 0) {
+        const lds_t* A = stage_buf(s);
+        abuf[0].sc = A[RG::kTokScaleOff + a_sc];
+        abuf[0].lo = *reinterpret_cast<const lds_v4i*>(A + a_lo);
+        abuf[0].hi = *reinterpret_cast<const lds_v4i*>(A + a_hi);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bw[k][i] =
+                *reinterpret_cast<const lds_v4i*>(A + RG::kWOff + b_op + 4096 * k + 1024 * i);
+            bs[k][i] = A[RG::kWScaleOff + b_sc + 256 * k + 64 * i];
+          }
+      }
+      asm volatile("" ::: "memory");
+    };
+    // Global load slot of MFMA m of tile j: with two or more tiles, the odd
+    // MFMAs of tiles 0 and 1 carry loads 0..3 and 4..; with one tile, MFMAs
+    // 0.. carry one each.
+    auto load_slot = [](int j, int m) constexpr -> int {
+      if (NJ == 1) return m < RG::kLoads ? m : -1;
+      if (j > 1 || !(m & 1)) return -1;
+      const int q = 4 * j + (m >> 1);
+      return q < RG::kLoads ? q : -1;
+    };
+    // One stage: per tile j, 8 MFMAs; after MFMAs 0..2 one read of tile
+    // j + 1's operands, and the global loads of stage s + kAhead in their
+    // slots.
+    auto compute = [&](int s) __attribute__((always_inline)) {
+      const lds_t* A = stage_buf(s);
+      if constexpr (NJ == 0) {
+#pragma unroll
+        for (int q = 0; q < RG::kLoads; ++q) issue_load(q, s + RG::kAhead);
+      } else {
+        auto tile_fn = [&](auto ji) __attribute__((always_inline)) {
+          constexpr int j = decltype(ji)::value;
+          AOp& cur = abuf[j & 1];
+          AOp& nxt = abuf[(j + 1) & 1];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int k = m >> 2, i = m & 3;
+            acc[j][k][i] = mfma_w4a8<0>(bw[k][i], cur.lo, cur.hi, acc[j][k][i], bs[k][i], cur.sc);
+            if constexpr (j + 1 < NJ) {
+              if (m == 0) nxt.sc = A[RG::kTokScaleOff + a_sc + 256 * (j + 1)];
+              if (m == 1) nxt.lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 8192 * (j + 1));
+              if (m == 2) nxt.hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 8192 * (j + 1));
+            }
+            if (load_slot(j, m) >= 0) issue_load(load_slot(j, m), s + RG::kAhead);
+          }
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+            if (j + 1 < NJ && m < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            if (load_slot(j, m) >= 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        };
+        static_for<0, NJ>(tile_fn);
+      }
+    };
+
+    constexpr int kInFlight = (RG::kAhead - 1) * RG::kLoads;
+#pragma unroll
+    for (int a = 0; a < RG::kAhead; ++a) {
+#pragma unroll
+      for (int q = 0; q < RG::kLoads; ++q) issue_load(q, a);
+      asm volatile("" ::: "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");   // stage 0's loads
+    asm volatile("s_barrier" ::: "memory");
+    read_start(0);
+    // Step s: the stage's MFMAs and stage s + kAhead's loads, the wait for
+    // stage s + 1 (issued kAhead - 1 steps back; the loads of the stages
+    // after it stay in flight), the barrier (stage s + 1 landed everywhere,
+    // stage s's buffer free), and stage s + 1's first operands.
+    for (int s = 0; s < n_stages; ++s) {
+      compute(s);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
+      asm volatile("s_barrier" ::: "memory");
+      if (s + 1 < n_stages) read_start(s + 1);
+    }
+    // Drain the reloads issued past the end before the ring is reused.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_barrier" ::: "memory");
+
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      pin_acc_agpr(acc[j][0]);
+      pin_acc_agpr(acc[j][1]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int t_in = 16 * (qt + 4 * j) + li;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        store_subtile<FC1>(p, acc[j][k], row_begin + t_in, t_in < n_valid, 4 * cg + 2 * hw + k, g);
+    }
+  };
+  // At most 64 P rows in use make at most 4 P tiles, so a wavefront
+  // holds at most P of them.
+  if constexpr (P == 1) {
+    if (nj == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+  } else if constexpr (P == 2) {
+    switch (nj) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      default: run(std::integral_constant<int, 2>{}); break;
+    }
+  } else {
+    switch (nj) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
+    }
+  }
+}
+
 template <bool FC1, bool TILED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fc_prefill_kernel(FcParams p, int n_cg) {
   // One LDS object: the stage ring, then the expert tile prefix and row
   // offsets (read once per workgroup), then the current item.
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
-  int* const prefix_s = reinterpret_cast<int*>(lds + kNumBuf * kStage);
+  int* const prefix_s = reinterpret_cast<int*>(lds + kRingBytes);
   int* const offs_s = prefix_s + kMaxLdsExperts + 1;
   int* const item_s = offs_s + kMaxLdsExperts + 1;
-  lds_t* const lds_base = (lds_t*)lds;   // LDS address space: immediate offsets fold
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wavefront
   const int hw = wave & 1, qt = wave >> 1;                     // weight half, token quarter
@@ -228,16 +467,17 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
   int32_t* const ctr = p.sched + xcd * kSchedStride;
   const __amdgpu_buffer_rsrc_t act_r = rsrc(p.act, (uint32_t)(p.act_rows * K));
 
-  // LDS read offsets (lane parts; the tile's part goes into the immediate):
-  // token tile tt = qt + 4 j at 2048 tt, its scale bytes at 64 tt; weight
-  // operand (unit 2 hw + k, block i) is 1 KB piece 4 (2 hw + k) + i, lane
-  // (li, g) at position 4 li + (g ^ ((li >> 1) & 3)); its scale byte is byte
-  // g of row 64 (2 hw + k) + 16 i + li's dword.
+  // LDS read offsets within a stage (lane parts; the tile's part and the
+  // stage layout's region offsets go into the immediate): token tile
+  // tt = qt + 4 j at 2048 tt, its scale bytes at 64 tt; weight operand
+  // (unit 2 hw + k, block i) is 1 KB piece 4 (2 hw + k) + i, lane (li, g) at
+  // position 4 li + (g ^ ((li >> 1) & 3)); its scale byte is byte g of row
+  // 64 (2 hw + k) + 16 i + li's dword.
   const int a_lo = 2048 * qt + li * kKS + 16 * (g ^ (li & 7));
   const int a_hi = 2048 * qt + li * kKS + 16 * ((4 + g) ^ (li & 7));
-  const int a_sc = kTokScaleOff + 64 * qt + 4 * li + g;
-  const int b_op = kWOff + 8192 * hw + 16 * (4 * li + (g ^ ((li >> 1) & 3)));
-  const int b_sc = kWScaleOff + 512 * hw + 4 * li + g;
+  const int a_sc = 64 * qt + 4 * li + g;
+  const int b_op = 8192 * hw + 16 * (4 * li + (g ^ ((li >> 1) & 3)));
+  const int b_sc = 512 * hw + 4 * li + g;
 
   // The workgroups of one XCD take its items in order from a shared counter,
   // so the items in flight are always a short run of neighbours (the column
@@ -300,23 +540,6 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
         w_voff[x] = (uint32_t)(rb + r) * (K / 2) + 16 * ch;
       }
     }
-    // LDS place of this wavefront's scale dwords.
-    const int s_lds = wave < 4 ? kTokScaleOff + 256 * wave : kWScaleOff + 256 * (wave - 4);
-    // Source rows of the token pieces (four per lane): all gather reads are
-    // issued before any is used, so their latencies overlap.  Rows past the
-    // expert's last repeat that row.
-    int src[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 32 * wave + 8 * i + (lane >> 3);
-      const int row = row_begin + min(tok, n_valid - 1);
-      src[i] = FC1 ? p.gather[row] : row;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      asm volatile("" : "+v"(src[i]));
-      if (FC1) src[i] /= p.top_k;
-    }
     if (wave < 4) {
       // The token scale dwords of stage s are the contiguous run
       // act_st[s][row_begin ..]: one coalesced piece per wavefront.
@@ -338,163 +561,16 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
       const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * u + 16 * (i & 1) : 64 * u + 16 * i;
       s_voff = (uint32_t)(rb + (r & 15)) * (K / 32);
     }
-    // Token rows: wavefront w fills rows 32 w + 8 i + l / 8 (i < 4); physical
-    // chunk l % 8 of a row takes logical chunk (l % 8) ^ (row & 7).  Rows of
-    // unused tiles get an offset past the buffer's end, which the buffer unit
-    // answers with zeros without touching memory (so every wavefront still
-    // issues the same loads).
-    uint32_t a_voff[4];
-    const int ac = (lane & 7) ^ ((lane >> 3) & 7);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 32 * wave + 8 * i + (lane >> 3);
-      a_voff[i] = tok < rows_used ? (uint32_t)src[i] * K + 16 * ac : kOutOfRange;
-    }
 
-    // Load q (0..6) of stage s_load into stage buffer s_load % 3: q < 4 a 1 KB
-    // piece of token rows, q = 4, 5 a weight piece, q = 6 the scale dwords.
-    auto issue_load = [&](int q, int s_load) __attribute__((always_inline)) {
-      asm volatile("" : "+s"(s_load));
-      const int sc = min(s_load, n_stages - 1);
-      uint8_t* base = lds + (s_load % kNumBuf) * kStage;
-      if (q < 4)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + 4096 * wave + 1024 * q, 16,
-                                                 a_voff[q], kKS * sc, 0, 0);
-      else if (q < 6)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_r, base + kWOff + 1024 * (2 * wave + q - 4), 16,
-                                                 w_voff[q - 4], w_step * sc, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_r, base + s_lds, 4, s_voff, s_step * sc, 0, 0);
-    };
-
-    // Stage buffer of stage s.  The offset is made opaque so that the compiler
-    // cannot prove later tiles' reads in bounds and hoist them.
-    auto stage_buf = [&](int s) __attribute__((always_inline)) {
-      int off = (s % kNumBuf) * kStage;
-      asm volatile("" : "+s"(off));
-      return static_cast<const lds_t*>(lds_base) + off;
-    };
-
-    // The stage loop for a wavefront holding NJ valid token tiles (a
-    // compile-time count, so no accumulator is conditionally updated).
-    auto run = [&](auto nji) __attribute__((always_inline)) {
-      constexpr int NJ = decltype(nji)::value;
-      v4f acc[NJ > 0 ? NJ : 1][2][4];  // [token tile j][unit k][row block i]
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[j][k][i] = v4f{0.f, 0.f, 0.f, 0.f};
-            asm volatile("" : "+a"(acc[j][k][i]));   // distinct registers from the start
-          }
-      AOp abuf[2];
-      v4i bw[2][4];   // weight operands of the stage: [unit k][row block i]
-      int bs[2][4];
-
-      // Operands of stage s's start: tile 0 and the weights.
-      auto read_start = [&](int s) __attribute__((always_inline)) {
-        if constexpr (NJ > 0) {
-          const lds_t* A = stage_buf(s);
-          abuf[0].sc = A[a_sc];
-          abuf[0].lo = *reinterpret_cast<const lds_v4i*>(A + a_lo);
-          abuf[0].hi = *reinterpret_cast<const lds_v4i*>(A + a_hi);
-#pragma unroll
-          for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              bw[k][i] = *reinterpret_cast<const lds_v4i*>(A + b_op + 4096 * k + 1024 * i);
-              bs[k][i] = A[b_sc + 256 * k + 64 * i];
-            }
-        }
-        asm volatile("" ::: "memory");
-      };
-      // Global load slot of MFMA m of tile j: with two or more tiles, the odd
-      // MFMAs of tiles 0 and 1 carry loads 0..3 and 4..6; with one tile,
-      // MFMAs 0..6 carry one each.
-      auto load_slot = [](int j, int m) constexpr -> int {
-        if (NJ == 1) return m < kLoadsPerStage ? m : -1;
-        if (j > 1 || !(m & 1)) return -1;
-        const int q = 4 * j + (m >> 1);
-        return q < kLoadsPerStage ? q : -1;
-      };
-      // One stage: per tile j, 8 MFMAs; after MFMAs 0..2 one read of tile
-      // j + 1's operands, and the global loads of stage s + 2 in their slots.
-      auto compute = [&](int s) __attribute__((always_inline)) {
-        const lds_t* A = stage_buf(s);
-        if constexpr (NJ == 0) {
-#pragma unroll
-          for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, s + 2);
-        } else {
-          auto tile_fn = [&](auto ji) __attribute__((always_inline)) {
-            constexpr int j = decltype(ji)::value;
-            AOp& cur = abuf[j & 1];
-            AOp& nxt = abuf[(j + 1) & 1];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-              const int k = m >> 2, i = m & 3;
-              acc[j][k][i] = mfma_w4a8<0>(bw[k][i], cur.lo, cur.hi, acc[j][k][i], bs[k][i], cur.sc);
-              if constexpr (j + 1 < NJ) {
-                if (m == 0) nxt.sc = A[a_sc + 256 * (j + 1)];
-                if (m == 1) nxt.lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 8192 * (j + 1));
-                if (m == 2) nxt.hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 8192 * (j + 1));
-              }
-              if (load_slot(j, m) >= 0) issue_load(load_slot(j, m), s + 2);
-            }
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
-              if (j + 1 < NJ && m < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-              if (load_slot(j, m) >= 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            }
-          };
-          static_for<0, NJ>(tile_fn);
-        }
-      };
-
-#pragma unroll
-      for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, 0);
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int q = 0; q < kLoadsPerStage; ++q) issue_load(q, 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerStage) : "memory");   // stage 0's loads
-      asm volatile("s_barrier" ::: "memory");
-      read_start(0);
-      // Step s: the stage's MFMAs and loads, the wait for stage s + 1 (its
-      // loads were issued one step back, followed by this step's 7), the
-      // barrier (stage s + 1 landed everywhere, stage s's buffer free), and
-      // stage s + 1's first operands.
-      for (int s = 0; s < n_stages; ++s) {
-        compute(s);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerStage) : "memory");
-        asm volatile("s_barrier" ::: "memory");
-        if (s + 1 < n_stages) read_start(s + 1);
-      }
-      // Drain the reloads issued past the end before the ring is reused.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      asm volatile("s_barrier" ::: "memory");
-
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        pin_acc_agpr(acc[j][0]);
-        pin_acc_agpr(acc[j][1]);
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int t_in = 16 * (qt + 4 * j) + li;
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          store_subtile<FC1>(p, acc[j][k], row_begin + t_in, t_in < n_valid, 4 * cg + 2 * hw + k, g);
-      }
-    };
-    switch (nj) {
-      case 0: run(std::integral_constant<int, 0>{}); break;
-      case 1: run(std::integral_constant<int, 1>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 3: run(std::integral_constant<int, 3>{}); break;
-      default: run(std::integral_constant<int, 4>{}); break;
-    }
+    // The rest depends on the stage layout, chosen by the rows in use.
+    const LaneGeom lg{wave, lane, hw, qt, g, li, a_lo, a_hi, a_sc, b_op, b_sc};
+    const ItemGeom it{cg, row_begin, n_valid, nj, rows_used, n_stages, K};
+    if (rows_used <= 64)
+      prefill_item<FC1, TILED, 1>(p, lds, lg, it, act_r, w_r, s_r, w_voff, s_voff, w_step, s_step);
+    else if (rows_used <= 128)
+      prefill_item<FC1, TILED, 2>(p, lds, lg, it, act_r, w_r, s_r, w_voff, s_voff, w_step, s_step);
+    else
+      prefill_item<FC1, TILED, 4>(p, lds, lg, it, act_r, w_r, s_r, w_voff, s_voff, w_step, s_step);
   }
 }
 
