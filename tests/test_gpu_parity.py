@@ -298,6 +298,28 @@ def test_one_hot_expert_spanning_many_tiles():
     _check_full(cfg, act, res, ref, "hot", w_np)
 
 
+@pytest.mark.parametrize("tiled", [True, False])
+def test_prefill_row_counts_at_layout_bounds(tiled):
+    # Experts whose row counts sit on both sides of the prefill kernel's
+    # 16-row tile, 64 / 128-row stage layouts and 256-row item bounds, their
+    # rows scattered over the tokens (K = 1).
+    counts = [1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320]
+    T = sum(counts)
+    cfg = synth.custom_config("bounds", 307, T=T, H=512, I=256, E=len(counts), K=1)
+    act, w_np, w_dev = _small_case(cfg)
+    rng = np.random.default_rng(307)
+    ids = rng.permutation(np.repeat(np.arange(len(counts), dtype=np.int32), counts))[:, None]
+    w = np.ones((T, 1), np.float32)
+    print(f"[bounds] T={T} H=512 I=256 E={len(counts)} tiled={tiled}", flush=True)
+    layer = _layer_for(cfg, w_dev, T, tiled=tiled)
+    x, logits, bias = _device_inputs(act)
+    res = run_steps(layer, x, logits, bias, torch.from_numpy(ids).to(DEV),
+                    torch.from_numpy(w).to(DEV))
+    assert np.array_equal(res["expert_offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    ref = _oracle_for(cfg, act, w_np, topk_idx=ids, topk_w=w)
+    _check_full(cfg, act, res, ref, "bounds", w_np)
+
+
 def test_route_ties_and_order():
     m = _lib()
     T, E, K = 6, 40, 5
