@@ -24,6 +24,10 @@
 //     past the last stage the final stage is reloaded to keep that count.
 //     The loads sit in MFMA slots early in the stage (the longest lead before
 //     their wait);
+//   * an expert with at most 64 rows takes two column groups per item, so the
+//     token rows loaded for a stage feed both weight tiles (the per-CU load
+//     path, not HBM, bounds these items; token rows were a third of their
+//     bytes);
 //   * the token scale dwords are first restaged (stage_scales_kernel) into a
 //     stage-major array in grouped-row order, so a tile's scales for one stage
 //     are one contiguous 1 KB run instead of one cache line per row: the
@@ -77,19 +81,33 @@ static_assert((16 << kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSize
 // P + 3 direct-to-LDS loads per stage (P token pieces, 2 weight pieces, the
 // token or the weight scale dwords); when stage s + 1 is waited for, the
 // loads of the kAhead - 1 stages after it stay in flight.
-template <int P>
+//
+// PAIR (P = 1 only): the item covers two column groups of an expert with at
+// most 64 rows, so one stage's token rows feed both weight tiles and the
+// token bytes per weight byte halve: [token rows 8 KB][token scale dwords
+// 2 KB][weights of both column groups 32 KB][their scale dwords 2 KB], 3
+// stages loaded 2 ahead.  Wavefront w works on column group w >> 2 of the
+// pair, weight half w & 1 and the token tiles (w >> 1) & 1 + 2 j; it issues
+// 7 loads per stage (a token piece, 4 weight pieces, a weight and a token
+// scale piece).
+template <int P, bool PAIR = false>
 struct Ring {
+  static_assert(!PAIR || P == 1, "pairs hold at most 64 rows");
+  static constexpr int kCG = PAIR ? 2 : 1;             // column groups per item
   static constexpr int kTokScaleOff = 64 * P * kKS;
-  static constexpr int kWOff = kTokScaleOff + kBM * 4;
-  static constexpr int kWScaleOff = kWOff + kBN * kKS / 2;
-  static constexpr int kStage = kWScaleOff + kBN * 4;
-  static constexpr int kNumBuf = P == 4 ? 3 : P == 2 ? 4 : 5;
+  static constexpr int kWOff = kTokScaleOff + kCG * kBM * 4;
+  static constexpr int kWScaleOff = kWOff + kCG * kBN * kKS / 2;
+  static constexpr int kStage = kWScaleOff + kCG * kBN * 4;
+  static constexpr int kNumBuf = PAIR ? 3 : P == 4 ? 3 : P == 2 ? 4 : 5;
   static constexpr int kAhead = kNumBuf - 1;
-  static constexpr int kLoads = P + 3;
+  static constexpr int kWPieces = 2 * kCG;             // weight pieces per wavefront and stage
+  static constexpr int kLoads = P + kWPieces + kCG;
+  static constexpr int kTileStep = PAIR ? 2 : 4;       // between a wavefront's token tiles
   static constexpr int kBytes = kNumBuf * kStage;
 };
-constexpr int kRingBytes = Ring<4>::kBytes;   // 153600, the largest of the three
-static_assert(Ring<2>::kBytes <= kRingBytes && Ring<1>::kBytes <= kRingBytes, "ring");
+constexpr int kRingBytes = Ring<4>::kBytes;   // 153600, the largest of the four
+static_assert(Ring<2>::kBytes <= kRingBytes && Ring<1>::kBytes <= kRingBytes &&
+              Ring<1, true>::kBytes <= kRingBytes, "ring");
 static_assert((Ring<1>::kAhead - 1) * Ring<1>::kLoads < 64, "vmcnt");
 constexpr int kLdsBytes = kRingBytes + 8 * (kMaxLdsExperts + 1) + 16;
 static_assert(kLdsBytes <= 160 * 1024, "LDS");
@@ -231,25 +249,29 @@ struct ItemGeom {
   int cg, row_begin, n_valid, nj, rows_used, n_stages, K;
 };
 
-// One item with stage layout Ring<P> (rows_used <= 64 P): token row
+// One item with stage layout Ring<P, PAIR> (rows_used <= 64 P): token row
 // offsets, the stage loop and the epilogue.  act_r / w_r / s_r are the
 // token-row, weight and scale buffers with this lane's offsets w_voff and
-// s_voff, advanced by w_step / s_step bytes per stage.
-template <bool FC1, bool TILED, int P>
+// s_voff, advanced by w_step / s_step bytes per stage (s_r: the wavefront's
+// token or weight scale dwords; with PAIR the weight scale dwords, and t_r
+// the token scale dwords).  it.cg is the wavefront's column group.
+template <bool FC1, bool TILED, int P, bool PAIR>
 __device__ __forceinline__ void prefill_item(const FcParams& p, uint8_t* lds, const LaneGeom& lg,
                                              const ItemGeom& it, __amdgpu_buffer_rsrc_t act_r,
                                              __amdgpu_buffer_rsrc_t w_r, __amdgpu_buffer_rsrc_t s_r,
-                                             const uint32_t (&w_voff)[2], uint32_t s_voff,
-                                             int w_step, int s_step) {
-  using RG = Ring<P>;
+                                             __amdgpu_buffer_rsrc_t t_r, const uint32_t (&w_voff)[4],
+                                             uint32_t s_voff, uint32_t t_voff, int w_step,
+                                             int s_step, int t_step) {
+  using RG = Ring<P, PAIR>;
   lds_t* const lds_base = (lds_t*)lds;
   const int wave = lg.wave, lane = lg.lane, hw = lg.hw, qt = lg.qt, g = lg.g, li = lg.li;
   const int a_lo = lg.a_lo, a_hi = lg.a_hi, a_sc = lg.a_sc, b_op = lg.b_op, b_sc = lg.b_sc;
   const int cg = it.cg, row_begin = it.row_begin, n_valid = it.n_valid, nj = it.nj;
   const int rows_used = it.rows_used, n_stages = it.n_stages, K = it.K;
   // LDS place of this wavefront's scale dwords.
-  const int s_lds =
-      wave < 4 ? RG::kTokScaleOff + 256 * wave : RG::kWScaleOff + 256 * (wave - 4);
+  const int s_lds = PAIR       ? RG::kWScaleOff + 256 * wave
+                    : wave < 4 ? RG::kTokScaleOff + 256 * wave
+                               : RG::kWScaleOff + 256 * (wave - 4);
   // Token rows: wavefront w fills rows 8 (P w + i) + l / 8 (i < P);
   // physical chunk l % 8 of a row takes logical chunk (l % 8) ^ (row & 7).
   // Source rows are all read before any is used, so the gather latencies
@@ -278,20 +300,24 @@ __device__ __forceinline__ void prefill_item(const FcParams& p, uint8_t* lds, co
   }
 
   // Load q of stage s_load into stage buffer s_load % kNumBuf: q < P a 1 KB
-  // piece of token rows, q = P, P + 1 a weight piece, q = P + 2 the scale
-  // dwords.
+  // piece of token rows, the next kWPieces a weight piece, then the scale
+  // dwords (with PAIR: the weight, then the token scale dwords).
   auto issue_load = [&](int q, int s_load) __attribute__((always_inline)) {
     asm volatile("" : "+s"(s_load));
     const int sc = min(s_load, n_stages - 1);
     uint8_t* base = lds + (s_load % RG::kNumBuf) * RG::kStage;
+    constexpr int nw = RG::kWPieces;
     if (q < P)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(act_r, base + 1024 * (P * wave + q), 16,
                                                a_voff[q], kKS * sc, 0, 0);
-    else if (q < P + 2)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_r, base + RG::kWOff + 1024 * (2 * wave + q - P),
+    else if (q < P + nw)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_r, base + RG::kWOff + 1024 * (nw * wave + q - P),
                                                16, w_voff[q - P], w_step * sc, 0, 0);
-    else
+    else if (!PAIR || q == P + nw)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s_r, base + s_lds, 4, s_voff, s_step * sc, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_r, base + RG::kTokScaleOff + 256 * wave, 4,
+                                               t_voff, t_step * sc, 0, 0);
   };
 
   // Stage buffer of stage s.  The offset is made opaque so that the compiler
@@ -365,9 +391,10 @@ __device__ __forceinline__ void prefill_item(const FcParams& p, uint8_t* lds, co
             const int k = m >> 2, i = m & 3;
             acc[j][k][i] = mfma_w4a8<0>(bw[k][i], cur.lo, cur.hi, acc[j][k][i], bs[k][i], cur.sc);
             if constexpr (j + 1 < NJ) {
-              if (m == 0) nxt.sc = A[RG::kTokScaleOff + a_sc + 256 * (j + 1)];
-              if (m == 1) nxt.lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 8192 * (j + 1));
-              if (m == 2) nxt.hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 8192 * (j + 1));
+              constexpr int t1 = RG::kTileStep * (j + 1);   // tiles past the wavefront's first
+              if (m == 0) nxt.sc = A[RG::kTokScaleOff + a_sc + 64 * t1];
+              if (m == 1) nxt.lo = *reinterpret_cast<const lds_v4i*>(A + a_lo + 2048 * t1);
+              if (m == 2) nxt.hi = *reinterpret_cast<const lds_v4i*>(A + a_hi + 2048 * t1);
             }
             if (load_slot(j, m) >= 0) issue_load(load_slot(j, m), s + RG::kAhead);
           }
@@ -413,15 +440,21 @@ __device__ __forceinline__ void prefill_item(const FcParams& p, uint8_t* lds, co
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int t_in = 16 * (qt + 4 * j) + li;
+      const int t_in = 16 * (qt + RG::kTileStep * j) + li;
 #pragma unroll
       for (int k = 0; k < 2; ++k)
         store_subtile<FC1>(p, acc[j][k], row_begin + t_in, t_in < n_valid, 4 * cg + 2 * hw + k, g);
     }
   };
   // At most 64 P rows in use make at most 4 P tiles, so a wavefront
-  // holds at most P of them.
-  if constexpr (P == 1) {
+  // holds at most P of them (with PAIR, at most 2).
+  if constexpr (PAIR) {
+    switch (nj) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      default: run(std::integral_constant<int, 2>{}); break;
+    }
+  } else if constexpr (P == 1) {
     if (nj == 0) run(std::integral_constant<int, 0>{});
     else run(std::integral_constant<int, 1>{});
   } else if constexpr (P == 2) {
@@ -492,6 +525,16 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     const int pe = __builtin_amdgcn_readfirstlane(prefix_s[e]);
     const int nt = __builtin_amdgcn_readfirstlane(prefix_s[e + 1]) - pe;
     const int local = item - pe * n_cg;
+    // An expert with at most 64 rows (one tile) runs as pairs of column
+    // groups: item i < n_cg / 2 of its range takes column groups 2 i and
+    // 2 i + 1, and the rest of its range is empty.
+    const int e_rows = __builtin_amdgcn_readfirstlane(offs_s[e + 1]) -
+                       __builtin_amdgcn_readfirstlane(offs_s[e]);
+    const bool pair = e_rows <= 64;
+    if (pair && local >= (n_cg >> 1)) {
+      __syncthreads();   // every wavefront has read item_s before it is rewritten
+      continue;
+    }
     // Items of an expert run in groups of kTileGroup tiles: within a group,
     // column group by column group, tile by tile.  The items in flight then
     // cover about 8 column groups x 4 tiles of a hot expert (its weights
@@ -499,7 +542,10 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     // 3 column groups x 10 tiles, which needs fewer bytes from memory.
     const int full = nt / kTileGroup, in_full = n_cg * kTileGroup * full;
     int cg, t_in_e;
-    if (local < in_full) {
+    if (pair) {
+      cg = 2 * local + (wave >> 2);   // this wavefront's column group
+      t_in_e = 0;
+    } else if (local < in_full) {
       const int grp = local / (n_cg * kTileGroup), r = local - grp * n_cg * kTileGroup;
       cg = r / kTileGroup;
       t_in_e = grp * kTileGroup + (r - cg * kTileGroup);
@@ -511,66 +557,97 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     const int row_begin = __builtin_amdgcn_readfirstlane(offs_s[e]) + t_in_e * kBM;
     const int n_valid = min(__builtin_amdgcn_readfirstlane(offs_s[e + 1]) - row_begin, kBM);
     const int ntiles = (n_valid + 15) >> 4;                      // 16-row tiles in use
-    const int nj = ntiles > qt ? (ntiles - qt + 3) >> 2 : 0;     // this wavefront's tiles
+    const int th = (wave >> 1) & 1;                              // token half of a pair item
+    const int nj = pair ? (ntiles > th ? (ntiles - th + 1) >> 1 : 0)
+                        : (ntiles > qt ? (ntiles - qt + 3) >> 2 : 0);   // this wavefront's tiles
     const int rows_used = 16 * ntiles;
 
     // Weight pieces: wavefront w copies 1 KB pieces c = 2 w, 2 w + 1 (unit
-    // c / 4, row block c % 4).  Scale dwords: wavefronts 0..3 copy token
-    // rows 64 w + l, wavefronts 4..7 weight rows 64 (w - 4) + l.
-    __amdgpu_buffer_rsrc_t w_r, s_r;
-    uint32_t w_voff[2], s_voff;
-    int w_step, s_step;
+    // c / 4, row block c % 4); of a pair, pieces c = 4 w .. 4 w + 3 of the
+    // two column groups' 32 pieces (column group c / 16).  Scale dwords:
+    // wavefronts 0..3 copy token rows 64 w + l, wavefronts 4..7 weight rows
+    // 64 (w - 4) + l; of a pair, wavefront w copies weight rows 64 w + l of
+    // the two column groups' 512 and token rows 64 w + l.
+    __amdgpu_buffer_rsrc_t w_r, s_r, t_r = act_r;
+    uint32_t w_voff[4] = {0u, 0u, 0u, 0u}, s_voff, t_voff = kOutOfRange;
+    int w_step, s_step, t_step = 0;
+    const int cg0 = pair ? 2 * local : cg;   // first column group of the item
+    const int nwp = pair ? 4 : 2;            // weight pieces per wavefront
     if (TILED) {
-      const size_t blk0 = tiled_block(e, cg >> 1, 0, n_cg >> 1, n_stages);
-      w_r = rsrc(p.w + blk0 * kTileBytes + 16384 * (cg & 1), (uint32_t)n_stages * kTileBytes);
+      const size_t blk0 = tiled_block(e, cg0 >> 1, 0, n_cg >> 1, n_stages);
+      w_r = rsrc(p.w + blk0 * kTileBytes + (pair ? 0 : 16384 * (cg & 1)),
+                 (uint32_t)n_stages * kTileBytes);
       w_step = kTileBytes;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) w_voff[x] = 1024 * (2 * wave + x) + 16 * lane;
+      for (int x = 0; x < 4; ++x) w_voff[x] = 1024 * (nwp * wave + x) + 16 * lane;
     } else {
-      const size_t e_rows = (size_t)e * p.N;
-      w_r = rsrc(p.w + e_rows * (K / 2), (uint32_t)p.N * (K / 2));
+      const size_t e_rows_off = (size_t)e * p.N;
+      w_r = rsrc(p.w + e_rows_off * (K / 2), (uint32_t)p.N * (K / 2));
       w_step = 64;
       // Position l of a piece holds row l / 4 of the block and logical
       // 16-byte chunk (l & 3) ^ ((l >> 3) & 3) (the tiled layout's order).
       const int r = lane >> 2, ch = (lane & 3) ^ ((lane >> 3) & 3);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int c = 2 * wave + x, u = 4 * cg + (c >> 2), i = c & 3;
+      for (int x = 0; x < 4; ++x) {
+        const int c = nwp * wave + x, u = 4 * (cg0 + (c >> 4)) + ((c & 15) >> 2), i = c & 3;
         const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * u + 16 * (i & 1) : 64 * u + 16 * i;
         w_voff[x] = (uint32_t)(rb + r) * (K / 2) + 16 * ch;
       }
     }
-    if (wave < 4) {
-      // The token scale dwords of stage s are the contiguous run
-      // act_st[s][row_begin ..]: one coalesced piece per wavefront.
-      s_r = rsrc(p.act_st, (uint32_t)(n_stages * p.n_routes * 4));
-      s_step = (int)(4 * p.n_routes);
+    // Token scale dwords of stage s: the contiguous run act_st[s][row_begin ..],
+    // one coalesced piece per wavefront.
+    const __amdgpu_buffer_rsrc_t st_r = rsrc(p.act_st, (uint32_t)(n_stages * p.n_routes * 4));
+    const int st_step = (int)(4 * p.n_routes);
+    if (pair) {
+      t_r = st_r;
+      t_step = st_step;
+      const int tok = 64 * wave + lane;
+      t_voff = tok < rows_used ? 4u * (uint32_t)(row_begin + tok) : kOutOfRange;
+    }
+    if (!pair && wave < 4) {
+      s_r = st_r;
+      s_step = st_step;
       const int tok = 64 * wave + lane;
       s_voff = tok < rows_used ? 4u * (uint32_t)(row_begin + tok) : kOutOfRange;
-    } else if (TILED) {
-      const size_t blk0 = tiled_block(e, cg >> 1, 0, n_cg >> 1, n_stages);
-      s_r = rsrc(p.w_s + blk0 * kTileScaleBytes + 1024 * (cg & 1),
-                 (uint32_t)n_stages * kTileScaleBytes);
-      s_step = kTileScaleBytes;
-      s_voff = 4 * (64 * (wave - 4) + lane);
     } else {
-      const size_t e_rows = (size_t)e * p.N;
-      s_r = rsrc(p.w_s + e_rows * (K / 32), (uint32_t)p.N * (K / 32));
-      s_step = 4;
-      const int r = 64 * (wave - 4) + lane, u = 4 * cg + (r >> 6), i = (r >> 4) & 3;
-      const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * u + 16 * (i & 1) : 64 * u + 16 * i;
-      s_voff = (uint32_t)(rb + (r & 15)) * (K / 32);
+      const int r = pair ? 64 * wave + lane : 64 * (wave - 4) + lane;   // of the item's rows
+      if (TILED) {
+        const size_t blk0 = tiled_block(e, cg0 >> 1, 0, n_cg >> 1, n_stages);
+        s_r = rsrc(p.w_s + blk0 * kTileScaleBytes + (pair ? 0 : 1024 * (cg & 1)),
+                   (uint32_t)n_stages * kTileScaleBytes);
+        s_step = kTileScaleBytes;
+        s_voff = 4 * r;
+      } else {
+        const size_t e_rows_off = (size_t)e * p.N;
+        s_r = rsrc(p.w_s + e_rows_off * (K / 32), (uint32_t)p.N * (K / 32));
+        s_step = 4;
+        const int rr = r & 255, u = 4 * (cg0 + (r >> 8)) + (rr >> 6), i = (rr >> 4) & 3;
+        const int rb = FC1 ? (i < 2 ? 0 : p.I) + 32 * u + 16 * (i & 1) : 64 * u + 16 * i;
+        s_voff = (uint32_t)(rb + (rr & 15)) * (K / 32);
+      }
     }
 
     // The rest depends on the stage layout, chosen by the rows in use.
-    const LaneGeom lg{wave, lane, hw, qt, g, li, a_lo, a_hi, a_sc, b_op, b_sc};
     const ItemGeom it{cg, row_begin, n_valid, nj, rows_used, n_stages, K};
-    if (rows_used <= 64)
-      prefill_item<FC1, TILED, 1>(p, lds, lg, it, act_r, w_r, s_r, w_voff, s_voff, w_step, s_step);
-    else if (rows_used <= 128)
-      prefill_item<FC1, TILED, 2>(p, lds, lg, it, act_r, w_r, s_r, w_voff, s_voff, w_step, s_step);
-    else
-      prefill_item<FC1, TILED, 4>(p, lds, lg, it, act_r, w_r, s_r, w_voff, s_voff, w_step, s_step);
+    if (pair) {
+      // Token tiles th, th + 2; the weight operands of column group w >> 2.
+      const int c = wave >> 2;
+      const LaneGeom lg{wave, lane, hw, th, g, li, a_lo - 2048 * (qt - th), a_hi - 2048 * (qt - th),
+                        a_sc - 64 * (qt - th), b_op + 16384 * c, b_sc + 1024 * c};
+      prefill_item<FC1, TILED, 1, true>(p, lds, lg, it, act_r, w_r, s_r, t_r, w_voff, s_voff,
+                                        t_voff, w_step, s_step, t_step);
+    } else {
+      const LaneGeom lg{wave, lane, hw, qt, g, li, a_lo, a_hi, a_sc, b_op, b_sc};
+      if (rows_used <= 64)
+        prefill_item<FC1, TILED, 1, false>(p, lds, lg, it, act_r, w_r, s_r, t_r, w_voff, s_voff,
+                                           t_voff, w_step, s_step, t_step);
+      else if (rows_used <= 128)
+        prefill_item<FC1, TILED, 2, false>(p, lds, lg, it, act_r, w_r, s_r, t_r, w_voff, s_voff,
+                                           t_voff, w_step, s_step, t_step);
+      else
+        prefill_item<FC1, TILED, 4, false>(p, lds, lg, it, act_r, w_r, s_r, t_r, w_voff, s_voff,
+                                           t_voff, w_step, s_step, t_step);
+    }
   }
 }
 
