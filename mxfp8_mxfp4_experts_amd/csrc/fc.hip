@@ -21,8 +21,9 @@
 // group b on both operands, and each weight-load instruction reads 64
 // contiguous bytes of each of 16 rows.
 //
-// Work decomposition: a workgroup (4 wavefronts) takes one tile of up to
-// 16*NT grouped rows of one expert and a column group of 4 units; a unit (one
+// Work decomposition: a workgroup (4 wavefronts) takes one tile of up to 32
+// grouped rows of one expert (one or two 16-row subtiles) and a column group
+// of 4 units; a unit (one
 // wavefront) is 64 weight rows: for FC1, gate rows [c, c+32) with up rows
 // [I+c, I+c+32), so SiTU and the 32-column requantisation group are local to
 // the lanes that hold them; for FC2, output columns [h, h+64).
@@ -42,6 +43,10 @@ namespace {
 #define DECODE_SJ 2
 #endif
 constexpr int kSJ = DECODE_SJ;
+
+// Tile list of the decode-shaped kernel: 32-row tiles (tile prefix 1).
+constexpr int kDecodeTilePrefixIndex = 1;
+constexpr int kDecodeTileRows = 16 << kDecodeTilePrefixIndex;
 
 // Operands of one super-step (kSJ 128-K slices) for one wavefront.
 template <int NT>
@@ -141,25 +146,12 @@ __device__ __forceinline__ void super_steps(v4f (&acc)[NT][4], const uint8_t* co
   if (S < n_super) compute_stage<NT>(acc, st0, g);
 }
 
-// Two-tile workgroups are held to two wavefronts per SIMD (a weight stream
-// in flight while the other wavefront's MFMAs issue).  One-tile workgroups
-// are left at the compiler's choice: two wavefronts at 176 VGPRs measured
-// faster than three at 168.
+// One tile of NT 16-row subtiles [row_begin, row_end) of expert e against
+// column group cg (one unit per wavefront).  STREAM: the expert has this one
+// tile, so its weights are read once.
 template <bool FC1, int NT, bool TILED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 1 : 2))) void
-fc_kernel(FcParams p) {
-  // Consecutive block ids land on different XCDs (round robin over 8); remap
-  // so that each XCD walks a contiguous range of (column group, tile) items,
-  // with the tiles of one expert adjacent and sharing its weights in L2.
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int logical = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  const int cg = logical / p.max_tiles, tile = logical % p.max_tiles;
-  const int* prefix = p.tile_prefix;
-  if (tile >= prefix[p.E_local]) return;
-  const int e = find_expert(prefix, p.E_local, tile);
-  const int row_begin = p.expert_offsets[e] + (tile - prefix[e]) * (16 * NT);
-  const int row_end = min(p.expert_offsets[e + 1], row_begin + 16 * NT);
-
+__device__ __forceinline__ void fc_tile(const FcParams& p, int e, int cg, int row_begin,
+                                        int row_end, bool stream_w) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int u = cg * 4 + wave;
   if (u >= p.n_units) return;
@@ -222,7 +214,7 @@ fc_kernel(FcParams p) {
   // tiles (whose workgroups run at about the same time on one XCD) keeps them
   // in L2 for its other tiles.
   const int n_super = K / (128 * kSJ);
-  if (prefix[e + 1] - prefix[e] == 1)
+  if (stream_w)
     super_steps<NT, TILED, true>(acc, wp, wsp, ap, asp, n_super, g);
   else
     super_steps<NT, TILED, false>(acc, wp, wsp, ap, asp, n_super, g);
@@ -263,6 +255,33 @@ fc_kernel(FcParams p) {
   }
 }
 
+// Tiles of up to 32 grouped rows (the 32-row tile list): a tile holding at
+// most 16 rows (every tile of an expert with at most 16) takes the one-subtile
+// path, a larger one the two-subtile path, so an expert with 17..32 rows reads
+// its weights once and one with fewer does no empty MFMAs.  Two wavefronts per
+// SIMD (256 VGPRs at most): one's weight stream is in flight while the
+// other's MFMAs issue.
+template <bool FC1, bool TILED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fc_kernel(
+    FcParams p) {
+  // Consecutive block ids land on different XCDs (round robin over 8); remap
+  // so that each XCD walks a contiguous range of (column group, tile) items,
+  // with the tiles of one expert adjacent and sharing its weights in L2.
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int logical = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  const int cg = logical / p.max_tiles, tile = logical % p.max_tiles;
+  const int* prefix = p.tile_prefix;
+  if (tile >= prefix[p.E_local]) return;
+  const int e = find_expert(prefix, p.E_local, tile);
+  const int row_begin = p.expert_offsets[e] + (tile - prefix[e]) * kDecodeTileRows;
+  const int row_end = min(p.expert_offsets[e + 1], row_begin + kDecodeTileRows);
+  const bool stream_w = prefix[e + 1] - prefix[e] == 1;
+  if (row_end - row_begin <= 16)
+    fc_tile<FC1, 1, TILED>(p, e, cg, row_begin, row_end, stream_w);
+  else
+    fc_tile<FC1, 2, TILED>(p, e, cg, row_begin, row_end, stream_w);
+}
+
 int expected_rows(int R, int E_local) {
   const int touched = R < E_local ? R : E_local;
   return touched > 0 ? R / touched : 1;
@@ -274,23 +293,18 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_
   const int avg = expected_rows(R, prm.E_local);
   if (avg >= 32 && prefill_shape_ok(prm, FC1))
     return launch_fc_prefill(FC1, tiled, prm, tile_prefix_all, n_cu, stream);
-  const int nt = avg <= 24 ? 1 : 2;
-  prm.tile_prefix = tile_prefix_all + (size_t)(nt == 1 ? 0 : 1) * (prm.E_local + 1);
-  const int tm = 16 * nt;
+  prm.tile_prefix = tile_prefix_all + (size_t)kDecodeTilePrefixIndex * (prm.E_local + 1);
   const int touched = R < prm.E_local ? R : prm.E_local;
-  prm.max_tiles = R / tm + touched;
+  prm.max_tiles = R / kDecodeTileRows + touched;
   const int groups = (prm.n_units + 3) / 4;
   const int64_t blocks = (int64_t)groups * prm.max_tiles;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(256);
-  if (tiled) {
-    if (nt == 1) hipLaunchKernelGGL((fc_kernel<FC1, 1, true>), grid, block, 0, stream, prm);
-    else hipLaunchKernelGGL((fc_kernel<FC1, 2, true>), grid, block, 0, stream, prm);
-  } else {
-    if (nt == 1) hipLaunchKernelGGL((fc_kernel<FC1, 1, false>), grid, block, 0, stream, prm);
-    else hipLaunchKernelGGL((fc_kernel<FC1, 2, false>), grid, block, 0, stream, prm);
-  }
+  if (tiled)
+    hipLaunchKernelGGL((fc_kernel<FC1, true>), grid, block, 0, stream, prm);
+  else
+    hipLaunchKernelGGL((fc_kernel<FC1, false>), grid, block, 0, stream, prm);
   return hipGetLastError();
 }
 
