@@ -16,6 +16,14 @@ constexpr int kGroup = 32;          // MX block: one E8M0 scale per 32 elements
 // FC tile heights (token rows per workgroup tile) for which moe_permute
 // writes a tile prefix: 16 << i for i in [0, kNumTileSizes).
 constexpr int kNumTileSizes = 5;
+// After the prefixes it writes the expert of every tile of height
+// 16 << kMapTileIndex (the decode-shaped FC kernels' tile list), so a
+// workgroup finds its expert with one load: at most R / 32 + E_local tiles
+// for R kept routes.
+constexpr int kMapTileIndex = 1;
+__host__ __device__ inline int64_t tile_map_entries(int64_t R, int E_local) {
+  return R / (16 << kMapTileIndex) + E_local;
+}
 
 // ---------------------------------------------------------------------------
 // Workspace layout shared by moe_permute / moe_fc1_situ / moe_fc2_combine.
@@ -32,7 +40,8 @@ inline int perm_chunks(int64_t R) {
 }
 
 struct WsLayout {
-  size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1]
+  size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1], then the tile -> expert map
+                        // int32 [tile_map_entries(T * top_k, E_local)]
   size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
   size_t fc_sched;      // int32 [9][kSchedStride]: per-XCD work counters of the prefill FC
                         // kernels, then their 9 item-range bounds
@@ -49,7 +58,8 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I) {
   WsLayout l;
   size_t off = 0;
   l.tile_prefix = off;
-  off = align256(off + sizeof(int32_t) * kNumTileSizes * (size_t)(E_local + 1));
+  off = align256(off + sizeof(int32_t) * (kNumTileSizes * (size_t)(E_local + 1) +
+                                          (size_t)tile_map_entries((int64_t)T * top_k, E_local)));
   l.perm_counts = off;
   off = align256(off + sizeof(int32_t) * (size_t)perm_chunks((int64_t)T * top_k) * E_local);
   l.fc_sched = off;

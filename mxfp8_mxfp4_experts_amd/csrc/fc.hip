@@ -44,9 +44,11 @@ namespace {
 #endif
 constexpr int kSJ = DECODE_SJ;
 
-// Tile list of the decode-shaped kernel: 32-row tiles (tile prefix 1).
+// Tile list of the decode-shaped kernel: 32-row tiles (tile prefix 1), whose
+// tile -> expert map the grouping step writes after the prefixes.
 constexpr int kDecodeTilePrefixIndex = 1;
 constexpr int kDecodeTileRows = 16 << kDecodeTilePrefixIndex;
+static_assert(kDecodeTilePrefixIndex == kMapTileIndex, "tile map");
 
 // Operands of one super-step (kSJ 128-K slices) for one wavefront.
 template <int NT>
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int cg = logical / p.max_tiles, tile = logical % p.max_tiles;
   const int* prefix = p.tile_prefix;
   if (tile >= prefix[p.E_local]) return;
-  const int e = find_expert(prefix, p.E_local, tile);
+  const int e = p.tile_map[tile];
   const int row_begin = p.expert_offsets[e] + (tile - prefix[e]) * kDecodeTileRows;
   const int row_end = min(p.expert_offsets[e + 1], row_begin + kDecodeTileRows);
   const bool stream_w = prefix[e + 1] - prefix[e] == 1;
@@ -294,6 +296,7 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_
   if (avg >= 32 && prefill_shape_ok(prm, FC1))
     return launch_fc_prefill(FC1, tiled, prm, tile_prefix_all, n_cu, stream);
   prm.tile_prefix = tile_prefix_all + (size_t)kDecodeTilePrefixIndex * (prm.E_local + 1);
+  prm.tile_map = tile_prefix_all + (size_t)kNumTileSizes * (prm.E_local + 1);
   const int touched = R < prm.E_local ? R : prm.E_local;
   prm.max_tiles = R / kDecodeTileRows + touched;
   const int groups = (prm.n_units + 3) / 4;

@@ -32,6 +32,7 @@ struct FcParams {
   int K, N, I;
   const int32_t* expert_offsets;
   const int32_t* tile_prefix;  // [E_local + 1] for this kernel's tile height
+  const int32_t* tile_map;     // expert of each tile (decode-shaped kernels' tile list)
   int E_local;
   int n_units, max_tiles;
   float alpha, beta;
@@ -82,16 +83,6 @@ __device__ __forceinline__ uint32_t e4m3x4_scaled(float x0, float x1, float x2, 
   v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x0, x1, s, false);
   v2s both = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x2, x3, s, true);
   return __builtin_bit_cast(uint32_t, both);
-}
-
-// Largest expert e with prefix[e] <= tile (the expert owning that tile).
-__device__ __forceinline__ int find_expert(const int* prefix, int E_local, int tile) {
-  int lo = 0, hi = E_local;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= tile) lo = mid; else hi = mid;
-  }
-  return lo;
 }
 
 // The MFMAs read operands from all 64 lanes: make the accumulators live here,

@@ -112,8 +112,9 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   int excl[kScanVals];
 #pragma unroll
   for (int v = 0; v < kScanVals; ++v) excl[v] = incl[v] - local[v] + wave_tot[wave][v];
-  // Then each expert's offset, its chunks' absolute starting rows and its
-  // tile prefixes.
+  // Then each expert's offset, its chunks' absolute starting rows, its
+  // tile prefixes and its entries of the tile -> expert map.
+  int32_t* const tile_map = tile_prefix + kNumTileSizes * (E_local + 1);
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     expert_offsets[e] = excl[0];
     int row = excl[0];
@@ -127,7 +128,10 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
 #pragma unroll
     for (int i = 0; i < kNumTileSizes; ++i) {
       tile_prefix[i * (E_local + 1) + e] = excl[1 + i];
-      excl[1 + i] += (total + (16 << i) - 1) >> (4 + i);
+      const int n = (total + (16 << i) - 1) >> (4 + i);
+      if (i == kMapTileIndex)
+        for (int t = 0; t < n; ++t) tile_map[excl[1 + i] + t] = e;
+      excl[1 + i] += n;
     }
   }
   const int n_kept = n_kept_s;

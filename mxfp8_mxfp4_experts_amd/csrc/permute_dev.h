@@ -87,6 +87,7 @@ __device__ __forceinline__ void permute_block(const IdxFn& idx_of, int R, int of
   int excl[kScanVals];
 #pragma unroll
   for (int v = 0; v < kScanVals; ++v) excl[v] = incl[v] - local[v] + wave_tot[wave][v];
+  int32_t* const tile_map = tile_prefix + kNumTileSizes * (E_local + 1);
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     int c = cnt[e];
     expert_offsets[e] = excl[0];
@@ -95,7 +96,10 @@ __device__ __forceinline__ void permute_block(const IdxFn& idx_of, int R, int of
 #pragma unroll
     for (int i = 0; i < kNumTileSizes; ++i) {
       tile_prefix[i * (E_local + 1) + e] = excl[1 + i];
-      excl[1 + i] += (c + (16 << i) - 1) >> (4 + i);
+      const int n = (c + (16 << i) - 1) >> (4 + i);
+      if (i == kMapTileIndex)
+        for (int t = 0; t < n; ++t) tile_map[excl[1 + i] + t] = e;
+      excl[1 + i] += n;
     }
   }
   __syncthreads();

@@ -196,6 +196,23 @@ def test_grouping_matches_oracle(T, K, E, E_local, offset):
     assert np.array_equal(to_np(sroute)[:n], r_sroute)
     assert np.all(to_np(sroute)[n:] == -1)
     assert np.array_equal(to_np(rrow), r_rrow)
+    _check_tile_schedule(ws, np.diff(r_offs), E_local)
+
+
+def _check_tile_schedule(ws, counts, E_local):
+    """The tile schedule at the workspace's start: per tile height 16 << i
+    (i < 5) the exclusive prefix of ceil(count / height) over the experts,
+    then the expert of every 32-row tile."""
+    words = to_np(ws.view(torch.int32))
+    for i in range(5):
+        tiles = (counts + (16 << i) - 1) // (16 << i)
+        ref = np.concatenate([[0], np.cumsum(tiles)])
+        got = words[i * (E_local + 1):(i + 1) * (E_local + 1)]
+        assert np.array_equal(got, ref), f"tile prefix {16 << i}"
+    tiles32 = (counts + 31) // 32
+    ref_map = np.repeat(np.arange(E_local, dtype=np.int32), tiles32)
+    start = 5 * (E_local + 1)
+    assert np.array_equal(words[start:start + len(ref_map)], ref_map), "tile -> expert map"
 
 
 @pytest.mark.parametrize("T,E,K,E_local,offset,H", [
@@ -231,8 +248,8 @@ def test_route_quant_permute_matches_separate_calls(T, E, K, E_local, offset, H)
                        ("xs", xs_a, xs_b), ("expert_offsets", offs_a, offs_b),
                        ("sorted_route", sr_a, sr_b), ("route_row", rr_a, rr_b)):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
-    n_prefix = 4 * 5 * (E_local + 1)        # the tile schedule at the workspace's start
-    assert torch.equal(ws_a[:n_prefix], ws_b[:n_prefix]), "tile prefix"
+    _check_tile_schedule(ws_a, np.diff(to_np(offs_a)), E_local)
+    _check_tile_schedule(ws_b, np.diff(to_np(offs_b)), E_local)
     r_idx, _ = oracle.route(logits, bias, K, 2.5)
     assert np.array_equal(to_np(idx_b), r_idx)
 
