@@ -232,8 +232,19 @@ __global__ __launch_bounds__(256) void stage_scales_kernel(const uint8_t* __rest
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= offs[E_local]) return;
   const int src = gather ? gather[r] / top_k : r;
-  const uint32_t* row = reinterpret_cast<const uint32_t*>(act_s + (size_t)src * k32);
-  for (int s = 0; s < n_stages; ++s) out[(size_t)s * R + r] = row[s];
+  const uint8_t* row = act_s + (size_t)src * k32;
+  int s = 0;
+  if ((k32 & 15) == 0) {
+    // 16-byte rows: four stages per load, all of a row's loads in flight.
+    for (; s + 4 <= n_stages; s += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + 4 * s);
+      out[(size_t)s * R + r] = v.x;
+      out[(size_t)(s + 1) * R + r] = v.y;
+      out[(size_t)(s + 2) * R + r] = v.z;
+      out[(size_t)(s + 3) * R + r] = v.w;
+    }
+  }
+  for (; s < n_stages; ++s) out[(size_t)s * R + r] = reinterpret_cast<const uint32_t*>(row)[s];
 }
 
 // Per-lane constants of a workgroup: wavefront, lane, weight half, token
