@@ -29,12 +29,11 @@ __host__ __device__ inline int64_t tile_map_entries(int64_t R, int E_local) {
 // Workspace layout shared by moe_permute / moe_fc1_situ / moe_fc2_combine.
 // Grouping (moe_permute): batches of at most kPermSingle routes take one
 // workgroup; larger ones are cut into chunks, one wavefront ranking each --
-// 256 routes per chunk up to 16384 routes (enough chunks to spread the
-// ranking), 2048 above (few enough that the per-expert scan over chunks
-// stays short).
+// 256 routes per chunk up to 16384 routes, 512 above (enough chunks to
+// spread the ranking; the per-expert scan over chunks reads them in batches).
 constexpr int kPermSingle = 2048;
 constexpr int kSchedStride = 64;   // int32 stride between the per-XCD work counters
-__host__ __device__ inline int perm_chunk_size(int64_t R) { return R <= 16384 ? 256 : 2048; }
+__host__ __device__ inline int perm_chunk_size(int64_t R) { return R <= 16384 ? 256 : 512; }
 inline int perm_chunks(int64_t R) {
   return R <= kPermSingle ? 0 : (int)((R + perm_chunk_size(R) - 1) / perm_chunk_size(R));
 }

@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
 
 // Chunk histograms -> per-chunk starting rows (in place), expert offsets,
 // tile prefixes; grouped rows past the kept count get -1.
+constexpr int kBatch = 16;
 __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
     int R, int E_local, int n_chunks, int32_t* __restrict__ counts,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_route,
@@ -76,8 +77,17 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
 #pragma unroll
   for (int v = 0; v < kScanVals; ++v) local[v] = 0;
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
+    // Chunk counts in batches of kBatch loads in flight (the chunks of one
+    // expert are a dependent chain otherwise).
     int total = 0;
-    for (int c = 0; c < n_chunks; ++c) total += counts[(size_t)c * E_local + e];
+    for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < n_chunks ? counts[(size_t)(c0 + j) * E_local + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) total += v[j];
+    }
     local[0] += total;
 #pragma unroll
     for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += (total + (16 << i) - 1) >> (4 + i);
@@ -118,10 +128,16 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     expert_offsets[e] = excl[0];
     int row = excl[0];
-    for (int c = 0; c < n_chunks; ++c) {
-      const int x = counts[(size_t)c * E_local + e];
-      counts[(size_t)c * E_local + e] = row;
-      row += x;
+    for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = c0 + j < n_chunks ? counts[(size_t)(c0 + j) * E_local + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (c0 + j < n_chunks) counts[(size_t)(c0 + j) * E_local + e] = row;
+        row += v[j];
+      }
     }
     const int total = row - excl[0];
     excl[0] = row;

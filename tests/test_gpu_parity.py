@@ -109,7 +109,7 @@ MID_SHAPES = [
     # spanning several tiles plus a partial last tile
     dict(T=600, H=1024, I=512, E=8, K=2),
     dict(T=700, H=768, I=256, E=32, K=4, E_local=8, expert_offset=16),
-    # more than one grouping chunk (2048 routes) and ~600 rows per expert
+    # more than 2048 routes (the chunked grouping path) and ~600 rows per expert
     dict(T=1200, H=512, I=256, E=6, K=3),
     # the largest top_k (64): every token routed to every expert
     dict(T=40, H=256, I=256, E=64, K=64),
@@ -174,8 +174,8 @@ def test_prepack_matches_documented_layout(which):
 @pytest.mark.parametrize("T,K,E,E_local,offset", [
     (200, 8, 600, 300, 100),      # one workgroup (at most 2048 routes)
     (700, 8, 600, 300, 100),      # 256-route chunks: 22, ragged last one
-    (5000, 8, 600, 300, 100),     # 2048-route chunks: 20, ragged last one
-    (4096, 16, 64, 64, 0),        # exactly 32 chunks, every expert hot
+    (5000, 8, 600, 300, 100),     # 512-route chunks: 79, ragged last one
+    (4096, 16, 64, 64, 0),        # exactly 128 chunks, every expert hot
 ])
 def test_grouping_matches_oracle(T, K, E, E_local, offset):
     """Grouping alone, bit-exact: masked slots, ids outside the local window
