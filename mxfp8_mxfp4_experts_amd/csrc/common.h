@@ -14,15 +14,20 @@ constexpr int kMaxTopK = 64;        // one wavefront lane per selected slot
 constexpr int kGroup = 32;          // MX block: one E8M0 scale per 32 elements
 
 // FC tile heights (token rows per workgroup tile) for which moe_permute
-// writes a tile prefix: 16 << i for i in [0, kNumTileSizes).
-constexpr int kNumTileSizes = 5;
+// writes a tile prefix: 32 << (3 i) for i in [0, kNumTileSizes), i.e. 32
+// (the decode-shaped FC kernels) and 256 (the prefill-shaped ones).
+constexpr int kNumTileSizes = 2;
+__host__ __device__ constexpr int tile_rows(int i) { return 32 << (3 * i); }
+__host__ __device__ inline int tiles_of(int rows, int i) {
+  return (rows + tile_rows(i) - 1) / tile_rows(i);
+}
 // After the prefixes it writes the expert of every tile of height
-// 16 << kMapTileIndex (the decode-shaped FC kernels' tile list), so a
+// tile_rows(kMapTileIndex) (the decode-shaped FC kernels' tile list), so a
 // workgroup finds its expert with one load: at most R / 32 + E_local tiles
 // for R kept routes.
-constexpr int kMapTileIndex = 1;
+constexpr int kMapTileIndex = 0;
 __host__ __device__ inline int64_t tile_map_entries(int64_t R, int E_local) {
-  return R / (16 << kMapTileIndex) + E_local;
+  return R / tile_rows(kMapTileIndex) + E_local;
 }
 
 // ---------------------------------------------------------------------------

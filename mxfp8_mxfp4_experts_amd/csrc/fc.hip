@@ -44,10 +44,11 @@ namespace {
 #endif
 constexpr int kSJ = DECODE_SJ;
 
-// Tile list of the decode-shaped kernel: 32-row tiles (tile prefix 1), whose
+// Tile list of the decode-shaped kernel: 32-row tiles (tile prefix 0), whose
 // tile -> expert map the grouping step writes after the prefixes.
-constexpr int kDecodeTilePrefixIndex = 1;
-constexpr int kDecodeTileRows = 16 << kDecodeTilePrefixIndex;
+constexpr int kDecodeTilePrefixIndex = 0;
+constexpr int kDecodeTileRows = tile_rows(kDecodeTilePrefixIndex);
+static_assert(kDecodeTileRows == 32, "two 16-row subtiles per tile");
 static_assert(kDecodeTilePrefixIndex == kMapTileIndex, "tile map");
 
 // Operands of one super-step (kSJ 128-K slices) for one wavefront.

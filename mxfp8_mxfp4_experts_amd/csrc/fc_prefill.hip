@@ -67,10 +67,10 @@ constexpr int kBM = 256;                     // token rows per tile
 constexpr int kBN = 256;                     // weight rows per tile (4 units)
 constexpr int kKS = 128;                     // K per stage
 constexpr int kThreads = 512;                // 8 wavefronts
-constexpr int kTilePrefixIndex = 4;          // tile height 16 << 4 = 256
+constexpr int kTilePrefixIndex = 1;          // tile height 256
 constexpr int kMaxLdsExperts = 1024;            // local experts whose metadata LDS holds
 static_assert(kKS == kTileK && 2 * kBN == kTileRows, "tile shape");
-static_assert((16 << kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSizes, "tile prefix");
+static_assert(tile_rows(kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileSizes, "tile prefix");
 
 // Stage layout of the LDS ring for an item whose used token rows fit in
 // 64 P (P = 4, 2 or 1 one-KB token pieces per wavefront and stage):

@@ -7,7 +7,8 @@
 // Result (both paths below give the same bytes): the kept routes of local
 // expert e occupy grouped rows [offs[e], offs[e+1]) in ascending route order;
 // sorted_route[row] = route, route_row[route] = row or -1; grouped rows past
-// the kept count hold -1; tile prefixes for the FC tile heights 16..256.
+// the kept count hold -1; tile prefixes for the FC tile heights 32 and 256 and
+// the expert of every 32-row tile.
 //
 // Small batches: one workgroup runs permute_block (permute_dev.h): a
 // histogram in LDS, block-wide scans of the counts and tile counts, then one
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
     }
     local[0] += total;
 #pragma unroll
-    for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += (total + (16 << i) - 1) >> (4 + i);
+    for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += tiles_of(total, i);
   }
   int incl[kScanVals];
 #pragma unroll
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
 #pragma unroll
     for (int i = 0; i < kNumTileSizes; ++i) {
       tile_prefix[i * (E_local + 1) + e] = excl[1 + i];
-      const int n = (total + (16 << i) - 1) >> (4 + i);
+      const int n = tiles_of(total, i);
       if (i == kMapTileIndex)
         for (int t = 0; t < n; ++t) tile_map[excl[1 + i] + t] = e;
       excl[1 + i] += n;

@@ -7,7 +7,8 @@
 // One workgroup of kPermThreads threads:
 //  1. histogram of local expert ids in LDS;
 //  2. block-wide exclusive scans of the counts and of the per-expert tile
-//     counts for the FC tile heights 16, 32, 64, 128 and 256 rows;
+//     counts for the FC tile heights (32 and 256 rows), and the expert of
+//     every 32-row tile;
 //  3. one wavefront walks the routes in ascending order, 64 at a time:
 //     lanes with the same expert find each other with ballots over the id
 //     bits, the lowest such lane reserves their rows from the expert's LDS
@@ -54,7 +55,7 @@ __device__ __forceinline__ void permute_block(const IdxFn& idx_of, int R, int of
     int c = cnt[e];
     local[0] += c;
 #pragma unroll
-    for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += (c + (16 << i) - 1) >> (4 + i);
+    for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += tiles_of(c, i);
   }
   // Inclusive wave scan, then scan of wave totals.
   int incl[kScanVals];
@@ -96,7 +97,7 @@ __device__ __forceinline__ void permute_block(const IdxFn& idx_of, int R, int of
 #pragma unroll
     for (int i = 0; i < kNumTileSizes; ++i) {
       tile_prefix[i * (E_local + 1) + e] = excl[1 + i];
-      const int n = (c + (16 << i) - 1) >> (4 + i);
+      const int n = tiles_of(c, i);
       if (i == kMapTileIndex)
         for (int t = 0; t < n; ++t) tile_map[excl[1 + i] + t] = e;
       excl[1 + i] += n;

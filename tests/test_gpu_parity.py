@@ -200,18 +200,19 @@ def test_grouping_matches_oracle(T, K, E, E_local, offset):
 
 
 def _check_tile_schedule(ws, counts, E_local):
-    """The tile schedule at the workspace's start: per tile height 16 << i
-    (i < 5) the exclusive prefix of ceil(count / height) over the experts,
-    then the expert of every 32-row tile."""
+    """The tile schedule at the workspace's start: per tile height (32 rows for
+    the decode-shaped FC kernels, 256 for the prefill-shaped ones) the
+    exclusive prefix of ceil(count / height) over the experts, then the expert
+    of every 32-row tile."""
     words = to_np(ws.view(torch.int32))
-    for i in range(5):
-        tiles = (counts + (16 << i) - 1) // (16 << i)
+    for i, height in enumerate((32, 256)):
+        tiles = (counts + height - 1) // height
         ref = np.concatenate([[0], np.cumsum(tiles)])
         got = words[i * (E_local + 1):(i + 1) * (E_local + 1)]
-        assert np.array_equal(got, ref), f"tile prefix {16 << i}"
+        assert np.array_equal(got, ref), f"tile prefix {height}"
     tiles32 = (counts + 31) // 32
     ref_map = np.repeat(np.arange(E_local, dtype=np.int32), tiles32)
-    start = 5 * (E_local + 1)
+    start = 2 * (E_local + 1)
     assert np.array_equal(words[start:start + len(ref_map)], ref_map), "tile -> expert map"
 
 
