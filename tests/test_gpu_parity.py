@@ -338,6 +338,31 @@ def test_prefill_row_counts_at_layout_bounds(tiled):
     _check_full(cfg, act, res, ref, "bounds", w_np)
 
 
+@pytest.mark.parametrize("tiled", [True, False])
+def test_decode_row_counts_at_tile_bounds(tiled):
+    # Few rows per expert on average (the decode-shaped kernel): experts whose
+    # row counts sit on both sides of its 16-row subtile and 32-row tile
+    # bounds, the rest of the 64 experts empty, rows scattered over the tokens.
+    counts = [1, 15, 16, 17, 31, 32, 33, 48, 64, 65]
+    E = 64
+    T = sum(counts)
+    cfg = synth.custom_config("dbounds", 308, T=T, H=512, I=256, E=E, K=1)
+    act, w_np, w_dev = _small_case(cfg)
+    rng = np.random.default_rng(308)
+    ids = rng.permutation(np.repeat(np.arange(len(counts), dtype=np.int32) * 5, counts))[:, None]
+    w = np.ones((T, 1), np.float32)
+    print(f"[dbounds] T={T} H=512 I=256 E={E} tiled={tiled}", flush=True)
+    layer = _layer_for(cfg, w_dev, T, tiled=tiled)
+    x, logits, bias = _device_inputs(act)
+    res = run_steps(layer, x, logits, bias, torch.from_numpy(ids).to(DEV),
+                    torch.from_numpy(w).to(DEV))
+    full = np.zeros(E, np.int64)
+    full[np.arange(len(counts)) * 5] = counts
+    assert np.array_equal(res["expert_offsets"], np.concatenate([[0], np.cumsum(full)]))
+    ref = _oracle_for(cfg, act, w_np, topk_idx=ids, topk_w=w)
+    _check_full(cfg, act, res, ref, "dbounds", w_np)
+
+
 def test_route_ties_and_order():
     m = _lib()
     T, E, K = 6, 40, 5
