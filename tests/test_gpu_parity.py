@@ -342,8 +342,9 @@ def test_prefill_row_counts_at_layout_bounds(tiled):
 def test_decode_row_counts_at_tile_bounds(tiled):
     # Few rows per expert on average (the decode-shaped kernel): experts whose
     # row counts sit on both sides of its 16-row subtile and 32-row tile
-    # bounds, the rest of the 64 experts empty, rows scattered over the tokens.
-    counts = [1, 15, 16, 17, 31, 32, 33, 48, 64, 65]
+    # bounds, and two spanning several tiles, the rest of the 64 experts empty,
+    # rows scattered over the tokens.
+    counts = [1, 15, 16, 17, 31, 32, 33, 48, 64, 65, 97, 130]
     E = 64
     T = sum(counts)
     cfg = synth.custom_config("dbounds", 308, T=T, H=512, I=256, E=E, K=1)
