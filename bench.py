@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -39,10 +40,19 @@ PAGES_EP_MIXED_MS = {128: 0.926, 512: 1.782, 2048: 4.355, 8192: 16.167}
 FC_SOURCES = ("common.h", "fc_common.h", "tiled.h", "fc.hip", "fc_prefill.hip")
 
 
+def _code_text(src):
+    """Source text without comments and blank space, so that a counter
+    record stays valid across edits that change no code."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def fc_source_sha():
     h = hashlib.sha256()
     for name in FC_SOURCES:
-        h.update(open(os.path.join(ROOT, "mxfp8_mxfp4_experts_amd", "csrc", name), "rb").read())
+        with open(os.path.join(ROOT, "mxfp8_mxfp4_experts_amd", "csrc", name)) as f:
+            h.update(_code_text(f.read()).encode())
     return h.hexdigest()
 
 

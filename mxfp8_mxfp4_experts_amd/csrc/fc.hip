@@ -23,10 +23,11 @@
 //
 // Work decomposition: a workgroup (4 wavefronts) takes one tile of up to 32
 // grouped rows of one expert (one or two 16-row subtiles) and a column group
-// of 4 units; a unit (one
-// wavefront) is 64 weight rows: for FC1, gate rows [c, c+32) with up rows
-// [I+c, I+c+32), so SiTU and the 32-column requantisation group are local to
-// the lanes that hold them; for FC2, output columns [h, h+64).
+// of 4 units; a unit (one wavefront) is 64 weight rows: for FC1, gate rows
+// [c, c+32) with up rows [I+c, I+c+32), so SiTU and the 32-column
+// requantisation group are local to the lanes that hold them; for FC2, output
+// columns [h, h+64).  The expert of each tile comes from the grouping step's
+// tile -> expert map.
 #include "common.h"
 #include "fc_common.h"
 #include "launch.h"
@@ -150,8 +151,8 @@ __device__ __forceinline__ void super_steps(v4f (&acc)[NT][4], const uint8_t* co
 }
 
 // One tile of NT 16-row subtiles [row_begin, row_end) of expert e against
-// column group cg (one unit per wavefront).  STREAM: the expert has this one
-// tile, so its weights are read once.
+// column group cg (one unit per wavefront).  stream_w: the expert has this one
+// tile, so its weights are read once and streamed past the caches.
 template <bool FC1, int NT, bool TILED>
 __device__ __forceinline__ void fc_tile(const FcParams& p, int e, int cg, int row_begin,
                                         int row_end, bool stream_w) {
