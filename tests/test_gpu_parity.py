@@ -338,6 +338,20 @@ def test_prefill_row_counts_at_layout_bounds(tiled):
     _check_full(cfg, act, res, ref, "bounds", w_np)
 
 
+def test_many_local_experts_with_many_rows():
+    # More local experts (1100) than the prefill-shaped kernel keeps in LDS,
+    # about 40 rows each: the decode-shaped kernel takes the whole layer, with
+    # experts spanning several tiles, and the grouping runs its chunked path.
+    cfg = synth.custom_config("wide", 309, T=2750, H=256, I=256, E=1100, K=16)
+    act, w_np, w_dev = _small_case(cfg)
+    print("[wide] T=2750 H=256 I=256 E=1100 K=16", flush=True)
+    layer = _layer_for(cfg, w_dev, cfg.T)
+    res = run_steps(layer, *_device_inputs(act))
+    ref = _oracle_for(cfg, act, w_np)
+    assert int(np.diff(res["expert_offsets"]).max()) > 32
+    _check_full(cfg, act, res, ref, "wide", w_np)
+
+
 @pytest.mark.parametrize("tiled", [True, False])
 def test_decode_row_counts_at_tile_bounds(tiled):
     # Few rows per expert on average (the decode-shaped kernel): experts whose
