@@ -48,13 +48,41 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 
 constexpr int kRegExpertsPerLane = 16;   // register path: E <= 1024
 
+// The lane's best two remaining keys among its experts lane + 64 j with bit j
+// of avail set: key descending, expert ascending among equal keys.
+struct Top2 {
+  uint32_t k0, k1, e0, e1;
+  bool has0, has1;
+};
+__device__ __forceinline__ Top2 lane_top2(const uint32_t (&key)[kRegExpertsPerLane],
+                                          uint32_t avail, int lane) {
+  Top2 t{0u, 0u, 0xFFFFFFFFu, 0xFFFFFFFFu, false, false};
+#pragma unroll
+  for (int j = 0; j < kRegExpertsPerLane; ++j) {
+    const bool a = (avail >> j) & 1u;
+    const uint32_t k = key[j], e = (uint32_t)(lane + 64 * j);
+    const bool first = a && (!t.has0 || k > t.k0);
+    const bool second = a && !first && (!t.has1 || k > t.k1);
+    t.k1 = first ? t.k0 : second ? k : t.k1;
+    t.e1 = first ? t.e0 : second ? e : t.e1;
+    t.has1 = first ? t.has0 : (second || t.has1);
+    t.k0 = first ? k : t.k0;
+    t.e0 = first ? e : t.e0;
+    t.has0 = t.has0 || first;
+  }
+  return t;
+}
+
 // One wavefront selects the top K of one token (E <= 64 * kRegExpertsPerLane)
-// from its keys in LDS.  Lane l holds the keys of experts l, l + 64, ...; each
-// of the K rounds takes the lane's best remaining key, the wavefront maximum of
-// those (DPP row shifts and broadcasts), then the smallest expert index among
-// the lanes holding that maximum; the owning lane retires the winner.  Lane
-// k < K returns slot k's expert and weight (s_k / sum_j s_j in double, times
-// scaling).  Every lane must call this.
+// from its keys in LDS.  Lane l holds the keys of experts l, l + 64, ... and a
+// cache of its best two remaining ones (key descending, expert ascending).
+// Each of the K rounds takes the wavefront maximum of the lanes' best keys
+// (DPP row shifts and broadcasts); the expert is read from the one lane
+// holding it, or, when several lanes hold that key, is the smallest expert
+// among them (a second reduction).  The owning lane retires the winner and
+// promotes its second key; only a lane that wins again before its cache is
+// refilled rescans its keys.  Lane k < K returns slot k's expert and weight
+// (s_k / sum_j s_j in double, times scaling).  Every lane must call this.
 __device__ __forceinline__ void select_topk_wave(const uint32_t* keys_s, const float* row, int E,
                                                  int K, float scaling, int lane, int& id_out,
                                                  float& w_out) {
@@ -66,18 +94,39 @@ __device__ __forceinline__ void select_topk_wave(const uint32_t* keys_s, const f
     key[j] = e < E ? keys_s[e] : 0u;
     avail |= (e < E ? 1u : 0u) << j;
   }
+  // Cache: c0 the best remaining key (has0 iff any remain), c1 the next one
+  // (valid while fresh1, until c0 is taken once).
+  Top2 c = lane_top2(key, avail, lane);
+  uint32_t k0 = c.k0, k1 = c.k1, e0 = c.e0, e1 = c.e1;
+  bool has0 = c.has0, has1 = c.has1, fresh1 = true;
   int my_id = 0;
   for (int k = 0; k < K; ++k) {
-    uint32_t best = 0, best_e = 0xFFFFFFFFu;
-#pragma unroll
-    for (int j = 0; j < kRegExpertsPerLane; ++j) {
-      const bool take = ((avail >> j) & 1u) && (best_e == 0xFFFFFFFFu || key[j] > best);
-      best = take ? key[j] : best;
-      best_e = take ? (uint32_t)(lane + 64 * j) : best_e;
+    const uint32_t ck = has0 ? k0 : 0u;
+    const uint32_t m = wave_max_u32(ck);
+    const bool cand = has0 && ck == m;
+    const uint64_t holders = __ballot(cand);
+    uint32_t win;
+    if (__popcll(holders) == 1)
+      win = (uint32_t)__builtin_amdgcn_readlane((int)e0, __ffsll((long long)holders) - 1);
+    else
+      win = wave_min_u32(cand ? e0 : 0xFFFFFFFFu);   // < E: K <= E
+    bool refill = false;
+    if ((int)(win & 63) == lane) {
+      avail &= ~(1u << (win >> 6));
+      if (fresh1) {
+        k0 = k1; e0 = e1; has0 = has1;
+        fresh1 = false;
+      } else {
+        refill = true;
+      }
     }
-    const uint32_t m = wave_max_u32(best);
-    const uint32_t win = wave_min_u32(best == m ? best_e : 0xFFFFFFFFu);   // < E: K <= E
-    if ((int)(win & 63) == lane) avail &= ~(1u << (win >> 6));
+    if (__ballot(refill)) {
+      if (refill) {
+        c = lane_top2(key, avail, lane);
+        k0 = c.k0; k1 = c.k1; e0 = c.e0; e1 = c.e1;
+        has0 = c.has0; has1 = c.has1; fresh1 = true;
+      }
+    }
     if (lane == k) my_id = (int)win;
   }
   my_id = (my_id >= 0 && my_id < E) ? my_id : 0;
