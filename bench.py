@@ -36,7 +36,7 @@ WORKLOADS = {"tiny": 0, "decode_T8": 1, "batched_decode_T256": 2, "prefill_T8192
 # -> median ms.  Another machine's figure: context for vs_baseline.
 PAGES_EP_MIXED_MS = {128: 0.926, 512: 1.782, 2048: 4.355, 8192: 16.167}
 
-# Sources of the FC kernels: a traffic figure is valid only for these bytes.
+# Sources of the FC kernels: a traffic figure is valid only for their code.
 FC_SOURCES = ("common.h", "fc_common.h", "tiled.h", "fc.hip", "fc_prefill.hip")
 
 
