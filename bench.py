@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rounds", type=int, default=1,
+                    help="timed rounds of --steps steps each; the step time is their median")
     ap.add_argument("--workload", default="decode_T8", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -192,19 +194,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(evs[i])
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(stop) / args.steps
-    fc1_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # Each round times exactly K steps between two events, bracketed by
+    # synchronisations; with several rounds the step time is their median.
+    round_ms, fc1_times, wall = [], [], 0.0
+    for _ in range(args.rounds):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(args.steps):
+            step(evs[i])
+        stop.record()
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        round_ms.append(start.elapsed_time(stop) / args.steps)
+        fc1_times += [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = float(np.median(round_ms))
+    fc1_ms = float(np.mean(fc1_times))
 
     # The timed calls must compute what the layer computes.
     ref = layer(x, logits, bias, topk_idx=idx.clone() if given else None,
@@ -275,6 +283,9 @@ def main():
                   "wall_s_timed": round(wall, 3)},
         "roofline": roof,
     }
+    if args.rounds > 1:
+        res["rounds"] = {"n": args.rounds, "ms_per_step": [round(v, 5) for v in round_ms],
+                         "max_over_min": round(max(round_ms) / min(round_ms), 4)}
     if not args.no_cpu_baseline:
         rid = idx.cpu().numpy()
         rw = tw.cpu().numpy()
