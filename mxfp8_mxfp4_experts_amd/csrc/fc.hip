@@ -128,26 +128,52 @@ __device__ __forceinline__ void compute_stage(v4f (&acc)[NT][4], const Stage<NT>
 
 // The super-step loop over K / (128 kSJ) steps.  No branch inside the loop:
 // the wait-count pass then lets the stage just loaded stay in flight while the
-// other stage's MFMAs issue.  When n_super is even the last iteration reloads
-// the final stage.
+// other stage's MFMAs issue.  Tiled layout: the last one or two steps run
+// after the loop, so no stage is loaded twice (the load path per CU is the
+// bound, and the reload was one super-step in 14 for FC2).  Checkpoint layout
+// (whose per-row pointers leave no registers for the peeled steps): the last
+// iteration reloads the final stage when n_super is even.
 template <int NT, bool TILED, bool STREAM>
 __device__ __forceinline__ void super_steps(v4f (&acc)[NT][4], const uint8_t* const* wp,
                                             const uint8_t* const* wsp, const uint8_t* const* ap,
                                             const uint8_t* const* asp, int n_super, int g) {
+  if (n_super <= 0) return;
   Stage<NT> st0, st1;
-  if (n_super > 0) load_stage<NT, TILED, STREAM>(st0, wp, wsp, ap, asp, 0, g);
+  load_stage<NT, TILED, STREAM>(st0, wp, wsp, ap, asp, 0, g);
   int S = 0;
-  for (; S + 1 < n_super; S += 2) {
+  if constexpr (!TILED) {
+    for (; S + 1 < n_super; S += 2) {
+      load_stage<NT, TILED, STREAM>(st1, wp, wsp, ap, asp, S + 1, g);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stage<NT>(acc, st0, g);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage<NT, TILED, STREAM>(st0, wp, wsp, ap, asp, min(S + 2, n_super - 1), g);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_stage<NT>(acc, st1, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (S < n_super) compute_stage<NT>(acc, st0, g);
+    return;
+  }
+  for (; S + 2 < n_super; S += 2) {
     load_stage<NT, TILED, STREAM>(st1, wp, wsp, ap, asp, S + 1, g);
     __builtin_amdgcn_sched_barrier(0);
     compute_stage<NT>(acc, st0, g);
     __builtin_amdgcn_sched_barrier(0);
-    load_stage<NT, TILED, STREAM>(st0, wp, wsp, ap, asp, min(S + 2, n_super - 1), g);
+    load_stage<NT, TILED, STREAM>(st0, wp, wsp, ap, asp, S + 2, g);
     __builtin_amdgcn_sched_barrier(0);
     compute_stage<NT>(acc, st1, g);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (S < n_super) compute_stage<NT>(acc, st0, g);
+  if (S + 1 < n_super) {
+    load_stage<NT, TILED, STREAM>(st1, wp, wsp, ap, asp, S + 1, g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<NT>(acc, st0, g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_stage<NT>(acc, st1, g);
+  } else {
+    compute_stage<NT>(acc, st0, g);
+  }
 }
 
 // One tile of NT 16-row subtiles [row_begin, row_end) of expert e against
