@@ -301,6 +301,40 @@ def test_masked_slots_empty_experts_and_idle_tokens():
     assert np.all(res["out_bits"][7] == 0)
 
 
+@pytest.mark.parametrize("T,tiled", [(8, True), (512, True), (512, False)])
+def test_no_route_kept_then_no_tokens(T, tiled):
+    """Degenerate grouping: every route lies outside the local window (or is
+    masked), so every local expert has zero rows and the FC kernels get no
+    tile (T = 8: decode-shaped path) or no item (T = 512: prefill path, whose
+    item ranges are then empty).  The output is all zeros, as in the oracle.
+    Then a call with no tokens: moe_permute still zeroes the expert offsets."""
+    cfg = synth.custom_config("none", 307, T=T, H=512, I=256, E=8, K=4, E_local=4,
+                              expert_offset=4)
+    act, w_np, w_dev = _small_case(cfg)
+    ids = np.tile(np.arange(cfg.K, dtype=np.int32), (T, 1))   # global ids 0..3: not local
+    ids[::3, 2] = -1
+    w = np.full((T, cfg.K), 0.25, np.float32)
+    print(f"[none] T={T} tiled={tiled} window [4, 8), ids in 0..3", flush=True)
+    layer = _layer_for(cfg, w_dev, T, tiled=tiled)
+    x, logits, bias = _device_inputs(act)
+    res = run_steps(layer, x, logits, bias, torch.from_numpy(ids).to(DEV),
+                    torch.from_numpy(w).to(DEV))
+    ref = _oracle_for(cfg, act, w_np, topk_idx=ids, topk_w=w)
+    assert np.all(ref["expert_offsets"] == 0) and np.all(ref["out"] == 0)
+    assert np.array_equal(res["xq"], ref["xq"]) and np.array_equal(res["xs"], ref["xs"])
+    assert np.all(res["expert_offsets"] == 0)
+    assert np.all(res["sorted_route"] == -1) and np.all(res["route_row"] == -1)
+    assert np.all(res["out_bits"] == 0)
+
+    layer.expert_offsets.fill_(7)
+    empty_ids = torch.empty((0, cfg.K), dtype=torch.int32, device=DEV)
+    empty_w = torch.empty((0, cfg.K), dtype=torch.float32, device=DEV)
+    out = layer(x[:0], logits[:0], bias, topk_idx=empty_ids, topk_w=empty_w)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, cfg.H)
+    assert np.all(to_np(layer.expert_offsets) == 0)
+
+
 def test_one_hot_expert_spanning_many_tiles():
     # every token routes to expert 2 in slot 0 (K = 1): one expert, many tiles
     cfg = synth.custom_config("hot", 301, T=333, H=256, I=256, E=4, K=1)
