@@ -19,15 +19,15 @@ import time
 
 import numpy as np
 
+import synth
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # dense MXFP8-rate scaled MFMA (f8 x f4 issues at this rate)
 
-WORKLOADS = {"tiny": 0, "decode_T8": 1, "batched_decode_T256": 2, "prefill_T8192": 3,
-             "ep_share_T4096": 4, "ckpt_ep32r7_M128": 5, "ckpt_ep32r7_M512": 6,
-             "ckpt_ep32r7_M2048": 7, "ckpt_ep32r7_M8192": 8}
+WORKLOADS = synth.WORKLOADS
 
 
 # The pages' own latency for the checkpoint-true "ep_mixed" runner workload
@@ -132,9 +132,8 @@ def main():
     import torch
 
     import mxfp8_mxfp4_experts_amd as m
-    import synth
 
-    cfg = synth.CONFIGS[WORKLOADS[args.workload]]
+    cfg = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     t_setup = time.perf_counter()
     if cfg.H == 7168:

@@ -69,22 +69,24 @@ class LayerConfig:
         return self.T * self.K
 
 
-# The five workloads: tiny, decode, batched decode, 8K prefill chunk, and one
-# GPU's expert-parallel share with Zipf-skewed load.
-CONFIGS = {
-    0: LayerConfig("tiny", 0, T=16, H=128, I=128, E=4, K=2, E_local=4),
-    1: LayerConfig("decode_T8", 1, T=8, H=7168, I=3584, E=896, K=16, E_local=896),
-    2: LayerConfig("batched_decode_T256", 2, T=256, H=7168, I=3584, E=896, K=16, E_local=896),
-    3: LayerConfig("prefill_T8192", 3, T=8192, H=7168, I=3584, E=896, K=16, E_local=896),
-    4: LayerConfig("ep_share_T4096", 4, T=4096, H=7168, I=3584, E=896, K=16, E_local=224,
-                   expert_offset=0, bias_kind="zipf"),
-}
-# The checkpoint-true expert shape with the pages' own benchmark routing (one
-# GPU of 32 holding experts [196, 224), 8 local + 8 remote slots per token),
-# at the four local batch sizes the pages measure.
+# The workloads by name (the second field is each one's seed-stream key):
+# tiny, decode, batched decode, 8K prefill chunk, and one GPU's
+# expert-parallel share with Zipf-skewed load ...
+_ALL = [
+    LayerConfig("tiny", 0, T=16, H=128, I=128, E=4, K=2, E_local=4),
+    LayerConfig("decode_T8", 1, T=8, H=7168, I=3584, E=896, K=16, E_local=896),
+    LayerConfig("batched_decode_T256", 2, T=256, H=7168, I=3584, E=896, K=16, E_local=896),
+    LayerConfig("prefill_T8192", 3, T=8192, H=7168, I=3584, E=896, K=16, E_local=896),
+    LayerConfig("ep_share_T4096", 4, T=4096, H=7168, I=3584, E=896, K=16, E_local=224,
+                expert_offset=0, bias_kind="zipf"),
+]
+# ... and the checkpoint-true expert shape with the pages' own benchmark
+# routing (one GPU of 32 holding experts [196, 224), 8 local + 8 remote slots
+# per token), at the four local batch sizes the pages measure.
 for _i, _m in enumerate((128, 512, 2048, 8192)):
-    CONFIGS[5 + _i] = LayerConfig(f"ckpt_ep32r7_M{_m}", 5 + _i, T=_m, H=3584, I=3072, E=896,
-                                  K=16, E_local=28, expert_offset=196, routing="ep_mixed")
+    _ALL.append(LayerConfig(f"ckpt_ep32r7_M{_m}", 5 + _i, T=_m, H=3584, I=3072, E=896,
+                            K=16, E_local=28, expert_offset=196, routing="ep_mixed"))
+WORKLOADS = {c.name: c for c in _ALL}
 
 
 def custom_config(name: str, key: int, **kw) -> LayerConfig:

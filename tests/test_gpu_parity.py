@@ -87,7 +87,7 @@ def _small_case(cfg):
 
 
 def test_tiny_config_all_steps():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["tiny"]
     act, w_np, w_dev = _small_case(cfg)
     print(f"[tiny] T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} K={cfg.K}", flush=True)
     layer = _layer_for(cfg, w_dev, cfg.T)
@@ -615,11 +615,12 @@ def _sample_tokens(ids, cfg, n):
     return sorted(set(picks))[:n] if n < 3 else sorted(set(picks))
 
 
-@pytest.mark.parametrize("cid,tiled", [(1, True), (2, True), (3, True), (4, True), (1, False),
-                                       (3, False)])
-def test_full_size_sampled(cid, tiled):
-    cfg = synth.CONFIGS[cid]
-    print(f"[full c{cid} tiled={tiled}] {cfg}", flush=True)
+@pytest.mark.parametrize("name,tiled", [("decode_T8", True), ("batched_decode_T256", True),
+                                        ("prefill_T8192", True), ("ep_share_T4096", True),
+                                        ("decode_T8", False), ("prefill_T8192", False)])
+def test_full_size_sampled(name, tiled):
+    cfg = synth.WORKLOADS[name]
+    print(f"[full {name} tiled={tiled}] {cfg}", flush=True)
     w_all = full_size_weights()
     sl = slice(cfg.expert_offset, cfg.expert_offset + cfg.E_local)
     w_dev = {k: v[sl] for k, v in w_all.items()}
@@ -642,7 +643,7 @@ def test_full_size_sampled(cid, tiled):
     none_kept = (rrow.reshape(cfg.T, cfg.K) < 0).all(1)
     assert np.all(res["out_bits"][none_kept] == 0)
     # FC1/FC2/combine on sampled tokens, one route at a time
-    toks = _sample_tokens(rid, cfg, 3 if cid != 1 else 2)
+    toks = _sample_tokens(rid, cfg, 3 if name != "decode_T8" else 2)
     cache = {}
 
     def weight_fn(e):
@@ -656,15 +657,15 @@ def test_full_size_sampled(cid, tiled):
         row = int(rrow[toks[j] * cfg.K + k])
         mism.append(byte_mismatch(res["hq"][row], hq_ref))
         deltas[row] = check_requant(res["hq"][row:row + 1], res["hs"][row:row + 1], a_ref[None],
-                                    hq_ref[None], hs_ref[None], f"c{cid} row {row}",
+                                    hq_ref[None], hs_ref[None], f"{name} row {row}",
                                     max_frac=5e-3)[0]
-    print(f"[full c{cid}] tokens {toks}: mean hq mismatch {np.mean(mism):.3g}", flush=True)
+    print(f"[full {name}] tokens {toks}: mean hq mismatch {np.mean(mism):.3g}", flush=True)
     assert np.mean(mism) <= 1e-3
     allow = flip_allowance(lambda row: deltas.get(row), toks, cfg.K, rrow, rw,
                            lambda row: np.searchsorted(offs, row, side="right") - 1,
                            lambda e: mxfp4_dequantize(to_np(w_dev["w2"][e]), to_np(w_dev["w2_s"][e])),
                            cfg.H)
-    assert_output_with_allowance(res["out"][toks], sub["out"], allow, f"full c{cid}")
+    assert_output_with_allowance(res["out"][toks], sub["out"], allow, f"full {name}")
 
 
 # ---------------------------------------------------------------------------
@@ -683,7 +684,7 @@ def _ckpt_weights(cfg):
 
 @pytest.mark.parametrize("tiled", [True, False])
 def test_ckpt_shape_M128_all_tokens(tiled):
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS["ckpt_ep32r7_M128"]
     print(f"[ckpt M128 tiled={tiled}] {cfg}", flush=True)
     act = synth.make_activations(cfg)
     w_dev = _ckpt_weights(cfg)
@@ -698,10 +699,10 @@ def test_ckpt_shape_M128_all_tokens(tiled):
     _check_full(cfg, act, res, ref, f"ckpt M128 tiled={tiled}", w_np)
 
 
-@pytest.mark.parametrize("cid", [7, 8])
-def test_ckpt_shape_large_M_sampled(cid):
-    cfg = synth.CONFIGS[cid]
-    print(f"[ckpt c{cid}] {cfg}", flush=True)
+@pytest.mark.parametrize("name", ["ckpt_ep32r7_M2048", "ckpt_ep32r7_M8192"])
+def test_ckpt_shape_large_M_sampled(name):
+    cfg = synth.WORKLOADS[name]
+    print(f"[{name}] {cfg}", flush=True)
     act = synth.make_activations(cfg)
     w_dev = _ckpt_weights(cfg)
     layer = _layer_for(cfg, w_dev, cfg.T)
@@ -727,12 +728,12 @@ def test_ckpt_shape_large_M_sampled(cid):
         row = int(rrow[toks[j] * cfg.K + k])
         mism.append(byte_mismatch(res["hq"][row], hq_ref))
         deltas[row] = check_requant(res["hq"][row:row + 1], res["hs"][row:row + 1], a_ref[None],
-                                    hq_ref[None], hs_ref[None], f"ckpt c{cid} row {row}",
+                                    hq_ref[None], hs_ref[None], f"{name} row {row}",
                                     max_frac=5e-3)[0]
-    print(f"[ckpt c{cid}] tokens {toks}: mean hq mismatch {np.mean(mism):.3g}", flush=True)
+    print(f"[{name}] tokens {toks}: mean hq mismatch {np.mean(mism):.3g}", flush=True)
     assert np.mean(mism) <= 1e-3
     allow = flip_allowance(lambda row: deltas.get(row), toks, cfg.K, rrow, rw,
                            lambda row: np.searchsorted(offs, row, side="right") - 1,
                            lambda e: mxfp4_dequantize(to_np(w_dev["w2"][e]), to_np(w_dev["w2_s"][e])),
                            cfg.H)
-    assert_output_with_allowance(res["out"][toks], sub["out"], allow, f"ckpt c{cid}")
+    assert_output_with_allowance(res["out"][toks], sub["out"], allow, f"{name}")

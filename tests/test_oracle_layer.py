@@ -48,7 +48,7 @@ def _assert_agree(o, b):
 
 
 def test_oracle_equals_bruteforce_tiny_config():
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["tiny"]
     case = synth.make_case(cfg)
     o, b = _run_both(cfg, case)
     _assert_agree(o, b)
@@ -282,7 +282,7 @@ def test_oracle_tokens_matches_full_layer_rows():
 def test_generator_weights_are_mxfp4_of_bf16_normals():
     # The input generator's bytes decode to values whose per-group absmax
     # sits in (3, 6] after scaling (smallest-scale rule), as the recipe says.
-    cfg = synth.CONFIGS[0]
+    cfg = synth.WORKLOADS["tiny"]
     wt = synth.make_expert_weights(cfg, experts=[0])
     v = C.mxfp4_dequantize(wt["w13"][0].numpy(), wt["w13_s"][0].numpy())
     sc = C.e8m0_decode(wt["w13_s"][0].numpy())

@@ -17,7 +17,7 @@ def _facts():
 def test_ep_mixed_configs_match_the_pages_benchmark():
     f = _facts()["ep_mixed_benchmark"]
     ck = _facts()["ep_mapping"]
-    cfgs = [c for c in synth.CONFIGS.values() if c.routing == "ep_mixed"]
+    cfgs = [c for c in synth.WORKLOADS.values() if c.routing == "ep_mixed"]
     assert [c.T for c in cfgs] == f["M"]
     for c in cfgs:
         assert (c.H, c.I, c.E, c.E_local, c.K) == (f["H"], f["I"], f["E"], f["E_local"], f["top_k"])
@@ -27,7 +27,7 @@ def test_ep_mixed_configs_match_the_pages_benchmark():
 
 def test_ep_mixed_routing_structure():
     f = _facts()["ep_mixed_benchmark"]
-    for c, avg in zip([c for c in synth.CONFIGS.values() if c.routing == "ep_mixed"][:2],
+    for c, avg in zip([c for c in synth.WORKLOADS.values() if c.routing == "ep_mixed"][:2],
                       f["avg_local_routes_per_expert"]):
         a = synth.make_activations(c)
         ids, w = a["topk_idx"], a["topk_w"]
@@ -44,7 +44,7 @@ def test_ep_mixed_routing_structure():
 def test_checkpoint_true_weight_shapes():
     """w13 = [w1; w3] and w2 of the local window have the checkpoint's shapes."""
     t = _facts()["checkpoint_expert_tensors"]
-    c = synth.CONFIGS[5]
+    c = synth.WORKLOADS["ckpt_ep32r7_M128"]
     small = synth.custom_config("shape", 0, T=1, H=c.H, I=c.I, E=c.E, K=1, E_local=1)
     w = synth.make_expert_weights(small, experts=[c.expert_offset])
     assert tuple(w["w13"].shape[1:]) == (2 * t["w1.weight_packed"][0], t["w1.weight_packed"][1])
