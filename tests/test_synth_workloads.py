@@ -51,3 +51,23 @@ def test_checkpoint_true_weight_shapes():
     assert tuple(w["w13_s"].shape[1:]) == (2 * t["w1.weight_scale"][0], t["w1.weight_scale"][1])
     assert tuple(w["w2"].shape[1:]) == tuple(t["w2.weight_packed"])
     assert tuple(w["w2_s"].shape[1:]) == tuple(t["w2.weight_scale"])
+
+
+def test_workload_table_names_keys_and_shapes():
+    """Each workload keeps its seed-stream key and its shape, so every drawn
+    input (and every stored figure measured on it) stays the same."""
+    want = {
+        "tiny": (0, 16, 128, 128, 4, 2, 4, 0),
+        "decode_T8": (1, 8, 7168, 3584, 896, 16, 896, 0),
+        "batched_decode_T256": (2, 256, 7168, 3584, 896, 16, 896, 0),
+        "prefill_T8192": (3, 8192, 7168, 3584, 896, 16, 896, 0),
+        "ep_share_T4096": (4, 4096, 7168, 3584, 896, 16, 224, 0),
+        "ckpt_ep32r7_M128": (5, 128, 3584, 3072, 896, 16, 28, 196),
+        "ckpt_ep32r7_M512": (6, 512, 3584, 3072, 896, 16, 28, 196),
+        "ckpt_ep32r7_M2048": (7, 2048, 3584, 3072, 896, 16, 28, 196),
+        "ckpt_ep32r7_M8192": (8, 8192, 3584, 3072, 896, 16, 28, 196),
+    }
+    assert list(synth.WORKLOADS) == list(want)
+    for name, c in synth.WORKLOADS.items():
+        assert c.name == name
+        assert (c.key, c.T, c.H, c.I, c.E, c.K, c.E_local, c.expert_offset) == want[name]
