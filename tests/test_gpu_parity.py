@@ -251,8 +251,11 @@ def test_route_quant_permute_matches_separate_calls(T, E, K, E_local, offset, H)
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
     _check_tile_schedule(ws_a, np.diff(to_np(offs_a)), E_local)
     _check_tile_schedule(ws_b, np.diff(to_np(offs_b)), E_local)
-    r_idx, _ = oracle.route(logits, bias, K, 2.5)
+    r_idx, r_w = oracle.route(logits, bias, K, 2.5)
     assert np.array_equal(to_np(idx_b), r_idx)
+    # routed scaling 2.5: the weights, scaled, against the oracle's too
+    ulp = np.abs(to_np(w_b).view(np.int32).astype(np.int64) - r_w.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 4, "routing weights with routed_scaling"
 
 
 @pytest.mark.parametrize("layout", ["up_gate", "interleaved"])
@@ -584,6 +587,19 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager), f"replay {i}"
         del other
+
+
+def test_routed_scaling_through_the_layer():
+    """A routed scaling factor other than 1 (page 5 routed scaling): the
+    routing weights carry it and the combined output scales with it."""
+    cfg = synth.custom_config("scaled", 308, T=24, H=256, I=128, E=8, K=3, routed_scaling=2.5)
+    act, w_np, w_dev = _small_case(cfg)
+    print("[scaled] T=24 H=256 I=128 E=8 K=3 routed_scaling=2.5", flush=True)
+    layer = _layer_for(cfg, w_dev, cfg.T)
+    res = run_steps(layer, *_device_inputs(act))
+    ref = _oracle_for(cfg, act, w_np)
+    assert np.allclose(ref["topk_w"].sum(1), 2.5, rtol=1e-6)
+    _check_full(cfg, act, res, ref, "scaled", w_np)
 
 
 def test_single_token_and_shrinking_batch():
