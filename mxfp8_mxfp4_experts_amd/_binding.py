@@ -126,7 +126,7 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, contiguous=True, device
 
 def _as_u16(x: torch.Tensor, name: str) -> torch.Tensor:
     if x.dtype == torch.bfloat16:
-        return x.view(torch.uint16) if x.is_contiguous() else x
+        return x.view(torch.uint16)   # same element size: any strides
     if x.dtype == torch.uint16:
         return x
     raise ValueError(f"{name} must be bfloat16 (or uint16 bf16 bits), got {x.dtype}")

@@ -602,6 +602,43 @@ def test_routed_scaling_through_the_layer():
     _check_full(cfg, act, res, ref, "scaled", w_np)
 
 
+def test_situ_parameters_other_than_the_checkpoints():
+    """SiTU with alpha = 2, beta = 10 (the calls take both as arguments; the
+    checkpoint fixes 4 and 25): the FC1 epilogue against the oracle's SiTU
+    with the same parameters."""
+    m = _lib()
+    cfg = synth.custom_config("situ", 309, T=24, H=256, I=256, E=8, K=3)
+    act, w_np, w_dev = _small_case(cfg)
+    print("[situ] T=24 H=256 I=256 E=8 K=3 alpha=2 beta=10", flush=True)
+    layer = m.MoELayer(w_dev["w13"], w_dev["w13_s"], w_dev["w2"], w_dev["w2_s"], top_k=cfg.K,
+                       E=cfg.E, situ_alpha=2.0, situ_beta=10.0, max_tokens=cfg.T)
+    res = run_steps(layer, *_device_inputs(act))
+    ref = _oracle_for(cfg, act, w_np, alpha=2.0, beta=10.0)
+    _check_full(cfg, act, res, ref, "situ", w_np)
+
+
+@pytest.mark.parametrize("T", [8, 40])
+def test_strided_activations_and_output(T):
+    """x and out as column windows of wider buffers (row strides H + 64,
+    ld_x and ld_out): the same output bytes as contiguous x and out, and the
+    columns outside the window untouched.  T = 8 takes the one-launch front,
+    T = 40 the three launches."""
+    cfg = synth.custom_config("strided", 310 + T, T=T, H=256, I=128, E=8, K=3)
+    act, w_np, w_dev = _small_case(cfg)
+    print(f"[strided] T={T} H=256 ld=320", flush=True)
+    layer = _layer_for(cfg, w_dev, cfg.T)
+    x, logits, bias = _device_inputs(act)
+    ref = layer(x, logits, bias)
+    wide_x = torch.zeros((T, cfg.H + 64), dtype=torch.bfloat16, device=DEV)
+    wide_x[:, 32:32 + cfg.H] = x
+    wide_out = torch.full((T, cfg.H + 64), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = wide_out[:, 16:16 + cfg.H]
+    layer(wide_x[:, 32:32 + cfg.H], logits, bias, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint16), ref.view(torch.uint16))
+    assert torch.all(wide_out[:, :16] == 3.0) and torch.all(wide_out[:, 16 + cfg.H:] == 3.0)
+
+
 def test_single_token_and_shrinking_batch():
     cfg = synth.custom_config("one", 303, T=1, H=256, I=128, E=8, K=3)
     act, w_np, w_dev = _small_case(cfg)
