@@ -511,6 +511,44 @@ def test_quant_exhaustive_bf16_patterns():
     assert not np.any(to_np(xs) == 0xFF)
 
 
+@pytest.mark.parametrize("T,E,K", [(12, 896, 16), (40, 2048, 8)])
+def test_route_without_bias(T, E, K):
+    """A NULL correction bias selects by the sigmoid scores alone: both routing
+    kernels (E up to 1024 in registers, wider from LDS) and the one-launch
+    front, against the oracle with no bias."""
+    m = _lib()
+    rng = np.random.default_rng(500 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    print(f"[nobias] T={T} E={E} K={K}", flush=True)
+    d_logits = torch.from_numpy(logits).to(DEV)
+    ids, w = m.moe_route(d_logits, None, K)
+    rid, rw = oracle.route(logits, None, K)
+    assert np.array_equal(to_np(ids), rid)
+    ulp = np.abs(to_np(w).view(np.int32).astype(np.int64) - rw.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 4
+    if E <= 1024:
+        x = torch.zeros((T, 128), dtype=torch.bfloat16, device=DEV)
+        ws = torch.zeros(m.moe_workspace_size(T, K, E, 128, 128), dtype=torch.uint8, device=DEV)
+        got = m.moe_route_quant_permute(d_logits, None, K, 1.0, x, 0, E, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(got[0]), rid)
+        assert torch.equal(got[1].view(torch.int32), w.view(torch.int32))
+
+
+@pytest.mark.parametrize("T,H", [(33, 160), (7, 32), (5, 96)])
+def test_quant_row_width_multiple_of_32(T, H):
+    """moe_quant_mxfp8 alone needs only H % 32 == 0: widths that are not
+    multiples of 128, against the oracle's bytes."""
+    m = _lib()
+    rng = np.random.default_rng(600 + H)
+    x = synth.f32_to_bf16_bits((rng.standard_normal((T, H)) *
+                                np.exp2(rng.integers(-20, 20, (T, 1)))).astype(np.float32))
+    print(f"[quant32] T={T} H={H}", flush=True)
+    xq, xs = m.moe_quant_mxfp8(torch.from_numpy(x.astype(np.int16)).to(DEV).view(torch.bfloat16))
+    rq, rs = oracle.quant_x(x)
+    assert np.array_equal(to_np(xq), rq) and np.array_equal(to_np(xs), rs)
+
+
 def test_deterministic_three_runs():
     cfg = synth.custom_config("det", 302, T=200, H=512, I=256, E=16, K=4)
     act, w_np, w_dev = _small_case(cfg)
