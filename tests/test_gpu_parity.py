@@ -549,6 +549,34 @@ def test_quant_row_width_multiple_of_32(T, H):
     assert np.array_equal(to_np(xq), rq) and np.array_equal(to_np(xs), rs)
 
 
+def test_two_layers_on_two_streams():
+    """The calls keep no state of their own (the prefill kernel's work
+    counters live in the caller's workspace): two layers with their own
+    buffers, running at the same time on two streams, give the bytes each
+    gives alone."""
+    cfg_a = synth.custom_config("streamA", 320, T=512, H=512, I=256, E=8, K=4)
+    cfg_b = synth.custom_config("streamB", 321, T=384, H=512, I=256, E=8, K=4)
+    act_a, _, w_dev = _small_case(cfg_a)
+    act_b = synth.make_activations(cfg_b)
+    print("[streams] T=512 / 384, H=512 I=256 E=8 K=4 (prefill path)", flush=True)
+    la, lb = _layer_for(cfg_a, w_dev, cfg_a.T), _layer_for(cfg_b, w_dev, cfg_b.T)
+    in_a, in_b = _device_inputs(act_a), _device_inputs(act_b)
+    ref_a, ref_b = la(*in_a).clone(), lb(*in_b).clone()
+    torch.cuda.synchronize()
+    out_a, out_b = torch.empty_like(ref_a), torch.empty_like(ref_b)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            la(*in_a, out=out_a)
+        with torch.cuda.stream(s2):
+            lb(*in_b, out=out_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.uint16), ref_a.view(torch.uint16))
+    assert torch.equal(out_b.view(torch.uint16), ref_b.view(torch.uint16))
+
+
 def test_deterministic_three_runs():
     cfg = synth.custom_config("det", 302, T=200, H=512, I=256, E=16, K=4)
     act, w_np, w_dev = _small_case(cfg)
