@@ -54,8 +54,10 @@ __global__ __launch_bounds__(kPermThreads) void front_kernel(
     }
   }
   __syncthreads();
+  // The grouping's LDS row of local experts reuses ids: each route's entry
+  // is read, then overwritten, by the same thread.
   permute_block([&](int r) { return ids[r]; }, T * K, offset, E_local, expert_offsets,
-                sorted_route, route_row, tile_prefix, cnt, cursor);
+                sorted_route, route_row, tile_prefix, cnt, cursor, ids, nullptr);
 }
 
 size_t front_lds_bytes(int T, int E, int K, int E_local) {

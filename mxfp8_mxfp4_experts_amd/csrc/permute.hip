@@ -32,7 +32,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int32_t* __restrict__ route_row, int32_t* __restrict__ tile_prefix) {
   extern __shared__ int lds_i[];
   permute_block([&](int r) { return idx[r]; }, R, offset, E_local, expert_offsets, sorted_route,
-                route_row, tile_prefix, lds_i, lds_i + E_local);
+                route_row, tile_prefix, lds_i, lds_i + E_local, lds_i + 2 * E_local,
+                E_local <= kPermWaveTableExperts ? lds_i + 2 * E_local + R : nullptr);
 }
 
 // Local expert of route r, or -1 (masked slot or outside the window).
@@ -206,7 +207,8 @@ hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, in
                           int32_t* sorted_route, int32_t* route_row, int32_t* tile_prefix,
                           int32_t* counts, hipStream_t stream) {
   if (R <= kPermSingle) {
-    const size_t lds = sizeof(int) * 2 * (size_t)E_local;
+    const size_t table = E_local <= kPermWaveTableExperts ? (size_t)kPermWaves * E_local : 0;
+    const size_t lds = sizeof(int) * (2 * (size_t)E_local + (size_t)R + table);
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, stream, idx, R, offset,
                        E_local, offs, sorted_route, route_row, tile_prefix);
     return hipGetLastError();

@@ -5,11 +5,15 @@
 // masked -1 slots and empty experts are part of the contract.
 //
 // One workgroup of kPermThreads threads:
-//  1. histogram of local expert ids in LDS;
+//  1. histogram of local expert ids in LDS, keeping each route's local
+//     expert (or -1) in LDS for step 3;
 //  2. block-wide exclusive scans of the counts and of the per-expert tile
 //     counts for the FC tile heights (32 and 256 rows), and the expert of
 //     every 32-row tile;
-//  3. one wavefront walks the routes in ascending order, 64 at a time:
+//  3. the routes are walked in ascending order, 64 at a time (their local
+//     experts read from LDS, so the walk waits on no global load); with a
+//     per-wavefront count table (small E_local) each wavefront walks its own
+//     contiguous slice from its own cursors, else one wavefront walks all:
 //     lanes with the same expert find each other with ballots over the id
 //     bits, the lowest such lane reserves their rows from the expert's LDS
 //     cursor, and each lane takes base + its rank among them.  This keeps
@@ -23,25 +27,38 @@ namespace mi355moe {
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / 64;
 constexpr int kScanVals = 1 + kNumTileSizes;
+// The per-wavefront count table (kPermWaves x E_local ints) is used up to
+// this many local experts (32 KB of LDS).
+constexpr int kPermWaveTableExperts = 512;
 
 // idx_of(r): global expert id of route r (r < R).  cnt, cursor: LDS int
-// [E_local] each.
+// [E_local] each; lrow: LDS int [R]; wtab: LDS int [kPermWaves][E_local], or
+// nullptr for the one-wavefront walk.
 template <typename IdxFn>
 __device__ __forceinline__ void permute_block(const IdxFn& idx_of, int R, int offset, int E_local,
                                               int32_t* __restrict__ expert_offsets,
                                               int32_t* __restrict__ sorted_route,
                                               int32_t* __restrict__ route_row,
                                               int32_t* __restrict__ tile_prefix, int* cnt,
-                                              int* cursor) {
+                                              int* cursor, int* lrow, int* wtab) {
   __shared__ int wave_tot[kPermWaves][kScanVals];
   __shared__ int n_kept_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Wavefront w of the walk takes routes [w * slice, (w + 1) * slice).
+  const int slice = ((R + kPermWaves - 1) / kPermWaves + 63) & ~63;
   for (int e = tid; e < E_local; e += kPermThreads) cnt[e] = 0;
+  if (wtab)
+    for (int i = tid; i < kPermWaves * E_local; i += kPermThreads) wtab[i] = 0;
   __syncthreads();
   for (int r = tid; r < R; r += kPermThreads) {
     int g = idx_of(r);
     int l = g - offset;
-    if (g >= 0 && l >= 0 && l < E_local) atomicAdd(&cnt[l], 1);
+    const bool kept = g >= 0 && l >= 0 && l < E_local;
+    if (kept) {
+      atomicAdd(&cnt[l], 1);
+      if (wtab) atomicAdd(&wtab[(r / slice) * E_local + l], 1);
+    }
+    lrow[r] = kept ? l : -1;
   }
   __syncthreads();
 
@@ -106,18 +123,29 @@ __device__ __forceinline__ void permute_block(const IdxFn& idx_of, int R, int of
   __syncthreads();
   const int n_kept = n_kept_s;
   for (int r = n_kept + tid; r < R; r += kPermThreads) sorted_route[r] = -1;
+  // Per-wavefront cursors: expert e's rows for wavefront w start after its
+  // rows from the slices before w.
+  if (wtab) {
+    for (int e = tid; e < E_local; e += kPermThreads) {
+      int run = cursor[e];
+      for (int w = 0; w < kPermWaves; ++w) {
+        const int c = wtab[w * E_local + e];
+        wtab[w * E_local + e] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+  }
+  int* const cur = wtab ? wtab + wave * E_local : cursor;
+  const int r_lo = wtab ? min(R, wave * slice) : 0;
+  const int r_hi = wtab ? min(R, r_lo + slice) : R;
 
-  if (wave == 0) {
+  if (wtab || wave == 0) {
     int nbits = 0;
     while ((1 << nbits) < E_local) ++nbits;
-    for (int base = 0; base < R; base += 64) {
+    for (int base = r_lo; base < r_hi; base += 64) {
       const int r = base + lane;
-      int l = -1;
-      if (r < R) {
-        int g = idx_of(r);
-        int ll = g - offset;
-        if (g >= 0 && ll >= 0 && ll < E_local) l = ll;
-      }
+      const int l = r < r_hi ? lrow[r] : -1;
       const bool kept = l >= 0;
       uint64_t peers = __ballot(kept);
       for (int bit = 0; bit < nbits; ++bit) {
@@ -130,14 +158,14 @@ __device__ __forceinline__ void permute_block(const IdxFn& idx_of, int R, int of
       const int leader = kept ? (__ffsll((long long)peers) - 1) : lane;
       int start = 0;
       if (kept && leader == lane) {
-        start = cursor[l];
-        cursor[l] = start + __popcll(peers);
+        start = cur[l];
+        cur[l] = start + __popcll(peers);
       }
       start = __shfl(start, leader);
-      if (r < R) {
+      if (r < r_hi) {
         if (kept) {
           const int pos = start + rank;
-          sorted_route[pos] = r;
+          if (pos < R) sorted_route[pos] = r;   // always true; keeps a stray row in bounds
           route_row[r] = pos;
         } else {
           route_row[r] = -1;

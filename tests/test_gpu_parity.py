@@ -172,7 +172,10 @@ def test_prepack_matches_documented_layout(which):
 
 
 @pytest.mark.parametrize("T,K,E,E_local,offset", [
-    (200, 8, 600, 300, 100),      # one workgroup (at most 2048 routes)
+    (200, 8, 600, 300, 100),      # one workgroup (at most 2048 routes), per-wavefront slices
+    (128, 16, 600, 512, 40),      # one workgroup, 2048 routes, the largest per-wavefront table
+    (120, 16, 1200, 700, 250),    # one workgroup, more experts: one wavefront walks all
+    (3, 2, 40, 30, 5),            # 6 routes: fifteen wavefronts with empty slices
     (700, 8, 600, 300, 100),      # 256-route chunks: 22, ragged last one
     (5000, 8, 600, 300, 100),     # 512-route chunks: 79, ragged last one
     (4096, 16, 64, 64, 0),        # exactly 128 chunks, every expert hot
