@@ -167,8 +167,8 @@ constexpr int kTileGroup = 4;   // tiles per item group of a multi-tile expert
 __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __restrict__ prefix,
                             int E_local, int n_cg, int32_t* __restrict__ bounds) {
   __shared__ long long cum_s[kMaxLdsExperts + 1];
-  __shared__ long long part_s[256];
-  const int tid = threadIdx.x;
+  __shared__ long long wsum_s[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = (E_local + 255) / 256, e0 = tid * per;
   long long mine = 0;
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
@@ -177,19 +177,19 @@ __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __r
     cum_s[e + 1] = w;   // turned into a running sum below
     mine += w;
   }
-  part_s[tid] = mine;
-  __syncthreads();
-  if (tid == 0) {
-    long long run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const long long v = part_s[i];
-      part_s[i] = run;
-      run += v;
-    }
-    cum_s[0] = 0;
+  // Exclusive scan of the 256 threads' sums: within each wavefront, then
+  // plus the totals of the wavefronts before it.
+  long long incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
+  if (lane == 63) wsum_s[wv] = incl;
+  if (tid == 0) cum_s[0] = 0;
   __syncthreads();
-  long long run = part_s[tid];
+  long long run = incl - mine;
+  for (int w = 0; w < wv; ++w) run += wsum_s[w];
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     run += cum_s[e + 1];
     cum_s[e + 1] = run;
