@@ -11,8 +11,10 @@
 // the expert of every 32-row tile.
 //
 // Small batches: one workgroup runs permute_block (permute_dev.h): a
-// histogram in LDS, block-wide scans of the counts and tile counts, then one
-// wavefront ranks the routes 64 at a time with ballots over the id bits.
+// histogram in LDS, block-wide scans of the counts and tile counts, then the
+// routes are ranked 64 at a time with ballots over the id bits (each
+// wavefront its own slice when a per-wavefront count table fits in LDS, else
+// one wavefront all of them).
 // Large batches: the routes are cut into chunks (perm_chunk_size); a count
 // kernel writes each chunk's histogram, one workgroup turns the histograms
 // into expert offsets, tile prefixes and each chunk's first row per expert,
