@@ -67,7 +67,9 @@ typedef enum moe_status {
   MOE_ERR_ALIGN = 3,           /* a pointer or stride is misaligned */
   MOE_ERR_WORKSPACE = 5,       /* workspace too small */
   MOE_ERR_HIP = 6,             /* a HIP runtime call or launch failed */
-  MOE_ERR_UNSUPPORTED_DEVICE = 7 /* current device is not gfx950 */
+  MOE_ERR_UNSUPPORTED_DEVICE = 7, /* current device is not gfx950 */
+  MOE_ERR_SCRATCH_LIMIT = 8    /* sizes need more than the library's static scratch
+                                  (moe_permute_noalloc only) */
 } moe_status_t;
 
 /* MOE_ABI_VERSION of the loaded library. */
@@ -130,6 +132,24 @@ moe_status_t moe_permute(const int32_t* topk_idx, int T, int top_k, int expert_o
                          int E_local, int32_t* expert_offsets, int32_t* sorted_route,
                          int32_t* route_row, void* workspace, size_t ws_bytes,
                          hipStream_t stream);
+
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments as moe_permute minus the workspace, and
+ * the same expert_offsets / sorted_route / route_row bytes.  It allocates
+ * nothing: the grouping's tile schedule and chunked histogram go to a
+ * library-owned device array of 4 MiB (4194304 bytes) that every GPU the
+ * library runs on holds until the process ends.
+ * Sizes whose schedule does not fit (the schedule part of
+ * moe_workspace_size: about 4 * (3 * E_local + T * top_k / 32) bytes plus
+ * 4 * E_local bytes per 256 or 512 routes above 2048 routes) return
+ * MOE_ERR_SCRATCH_LIMIT before anything is launched.  Every call on one GPU
+ * shares that GPU's array, so calls that overlap on one GPU (several streams
+ * or threads) race; the FC calls cannot use this call's schedule (they read
+ * the one moe_permute writes into their workspace). */
+moe_status_t moe_permute_noalloc(const int32_t* topk_idx, int T, int top_k, int expert_offset,
+                                 int E_local, int32_t* expert_offsets, int32_t* sorted_route,
+                                 int32_t* route_row, hipStream_t stream);
 
 /* a1 + a2 + a3 in one call (decode latency: page 1 "Serving call chain" runs
  * routing, quantisation and grouping before the expert GEMMs; their fixed

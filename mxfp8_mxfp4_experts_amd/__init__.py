@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     moe_fc1_situ,
     moe_fc2_combine,
     moe_permute,
+    moe_permute_noalloc,
     W13_GATE_UP,
     W13_INTERLEAVED,
     W13_UP_GATE,

@@ -20,6 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi355mo
 MOE_STATUS = {
     0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
     5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED_DEVICE",
+    8: "MOE_ERR_SCRATCH_LIMIT",
 }
 
 # Entry points declared in include/mi355moe.h.
@@ -27,7 +28,7 @@ EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_route", "moe_quant_mxfp8",
     "moe_permute", "moe_fc1_situ", "moe_fc2_combine", "moe_prepack_w13", "moe_prepack_w2",
     "moe_fc1_situ_tiled", "moe_fc2_combine_tiled", "moe_route_quant_permute",
-    "moe_prepack_w13_layout",
+    "moe_prepack_w13_layout", "moe_permute_noalloc",
 )
 
 # moe_w13_layout_t values (row order of a w13 tensor)
@@ -58,6 +59,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.moe_quant_mxfp8.argtypes = [_P, _I64, _I, _I, _P, _P, _P]
     lib.moe_permute.restype = _I
     lib.moe_permute.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]
+    lib.moe_permute_noalloc.restype = _I
+    lib.moe_permute_noalloc.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P]
     lib.moe_route_quant_permute.restype = _I
     lib.moe_route_quant_permute.argtypes = [_P, _I64, _P, _I, _I, _I, _F, _P, _I64, _I, _I, _I,
                                             _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
@@ -252,6 +255,30 @@ def moe_permute(topk_idx: torch.Tensor, expert_offset: int, E_local: int, worksp
                                             _ptr(expert_offsets), _ptr(sorted_route),
                                             _ptr(route_row), _ptr(workspace), workspace.numel(),
                                             _stream()))
+    return expert_offsets, sorted_route, route_row
+
+
+def moe_permute_noalloc(topk_idx: torch.Tensor, expert_offset: int, E_local: int,
+                        expert_offsets=None, sorted_route=None, route_row=None):
+    """moe_permute without a workspace (the library's static scratch holds
+    the schedule); same grouping outputs."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, top_k]")
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    if expert_offsets is None:
+        expert_offsets = torch.empty(E_local + 1, dtype=torch.int32, device=dev)
+    if sorted_route is None:
+        sorted_route = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if route_row is None:
+        route_row = torch.empty(T * K, dtype=torch.int32, device=dev)
+    _need(expert_offsets, "expert_offsets", torch.int32, (E_local + 1,), device=dev)
+    _need(sorted_route, "sorted_route", torch.int32, (T * K,), device=dev)
+    _need(route_row, "route_row", torch.int32, (T * K,), device=dev)
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        _ptr(topk_idx), T, K, expert_offset, E_local, _ptr(expert_offsets), _ptr(sorted_route),
+        _ptr(route_row), _stream()))
     return expert_offsets, sorted_route, route_row
 
 

@@ -71,6 +71,8 @@ const char* moe_strerror(int status) {
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case MOE_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "sizes need more than the no-allocation entry point's static scratch";
     default: return "unknown status";
   }
 }

@@ -41,7 +41,7 @@ def test_library_exports_every_header_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert lib.moe_abi_version() == 1
-    for code in (0, 1, 2, 3, 5, 6, 7):
+    for code in (0, 1, 2, 3, 5, 6, 7, 8):
         assert lib.moe_strerror(code)
     assert lib.moe_strerror(99) == b"unknown status"
 
@@ -162,3 +162,16 @@ def test_binding_rejects_cpu_tensors():
         B.moe_route(torch.zeros(4, 8), None, 2)
     with pytest.raises(ValueError):
         B.moe_quant_mxfp8(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+def test_permute_noalloc_validation(lib):
+    p = lib.moe_permute_noalloc
+    assert p(FAKE, 4, 0, 0, 8, FAKE, FAKE, FAKE, None) == 2                # top_k 0
+    assert p(FAKE, 4, 2, -1, 8, FAKE, FAKE, FAKE, None) == 2               # offset < 0
+    assert p(FAKE, 4, 2, 0, 5000, FAKE, FAKE, FAKE, None) == 2             # E_local > 4096
+    assert p(None, 4, 2, 0, 8, FAKE, FAKE, FAKE, None) == 1                # null ids
+    assert p(FAKE, 4, 2, 0, 8, None, FAKE, FAKE, None) == 1                # null offsets
+    assert p(FAKE, 4, 2, 0, 8, MIS, FAKE, FAKE, None) == 3
+    # 2^18 routes over 4096 local experts need an 8 MiB schedule: past the
+    # 4 MiB static scratch, refused before any HIP call.
+    assert p(FAKE, 16384, 16, 0, 4096, FAKE, FAKE, FAKE, None) == 8
