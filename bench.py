@@ -186,8 +186,9 @@ def main():
                        layer.workspace, cfg.situ_alpha, cfg.situ_beta, hq, hs, tiled=layer.tiled)
         if ev is not None:
             ev[1].record()
-        B.moe_fc2_combine(hq, hs, T, K, layer.expert_offsets, rrow, tw, layer.w2, layer.w2_s,
-                          layer.workspace, out, tiled=layer.tiled)
+        B.moe_fc2_combine(hq, hs, T, K, layer.expert_offsets, sroute, rrow, tw, layer.w2,
+                          layer.w2_s, layer.workspace, out, tiled=layer.tiled,
+                          mode=layer.combine_mode)
 
     for _ in range(args.warmup):
         step()

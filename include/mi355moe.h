@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes have fixed values (page 1 records a Python/C++ enum mismatch
  * that silently turned SiTU into a non-gated activation; these values never
@@ -65,12 +65,31 @@ typedef enum moe_status {
   MOE_ERR_NULL = 1,            /* a required pointer is NULL */
   MOE_ERR_SHAPE = 2,           /* a size or stride is out of range */
   MOE_ERR_ALIGN = 3,           /* a pointer or stride is misaligned */
+  MOE_ERR_ENUM = 4,            /* an enum argument has no defined value */
   MOE_ERR_WORKSPACE = 5,       /* workspace too small */
   MOE_ERR_HIP = 6,             /* a HIP runtime call or launch failed */
   MOE_ERR_UNSUPPORTED_DEVICE = 7, /* current device is not gfx950 */
   MOE_ERR_SCRATCH_LIMIT = 8    /* sizes need more than the library's static scratch
                                   (moe_permute_noalloc only) */
 } moe_status_t;
+
+/* How moe_fc2_combine sums the top-k FC2 rows of a token (fixed values).
+ * Page 1 ("Serving call chain": finalize after GEMM2; "Phase 2 correctness
+ * harness" / symmetry constraints) describes both: a fused finalize that
+ * accumulates with atomics, whose order and so whose float rounding vary
+ * from run to run, and the non-fused finalize kept for bitwise-repeatable
+ * results.
+ *   MOE_COMBINE_DETERMINISTIC  FC2 writes each kept route's row to the
+ *       workspace; a second kernel sums a token's rows in slot order.
+ *       Bitwise repeatable.  The default.
+ *   MOE_COMBINE_ATOMIC  the FC2 epilogue adds topk_w * row into a float
+ *       [T, H] sum in the workspace with atomic adds (cleared first in the
+ *       same call), then one pass rounds it to bf16.  Same bar against the
+ *       definition, not bitwise repeatable. */
+typedef enum moe_combine {
+  MOE_COMBINE_DETERMINISTIC = 0,
+  MOE_COMBINE_ATOMIC = 1
+} moe_combine_t;
 
 /* MOE_ABI_VERSION of the loaded library. */
 int moe_abi_version(void);
@@ -79,11 +98,12 @@ int moe_abi_version(void);
 const char* moe_strerror(int status);
 
 /* Bytes of workspace that moe_permute, moe_fc1_situ and moe_fc2_combine need
- * for a layer call with these sizes (one buffer serves all three; moe_permute
- * writes the FC kernels' tile schedule into it and moe_fc2_combine keeps the
- * per-route FC2 rows there, so pass the same buffer to all three).
- * Returns 0 for invalid sizes. */
-size_t moe_workspace_size(int T, int top_k, int E_local, int H, int I);
+ * for a layer call with these sizes and combine mode (one buffer serves all
+ * three; moe_permute writes the FC kernels' tile schedule into it and
+ * moe_fc2_combine keeps the per-route FC2 rows, or with MOE_COMBINE_ATOMIC the
+ * float [T, H] sums, there, so pass the same buffer to all three).
+ * Returns 0 for invalid sizes or an unknown mode. */
+size_t moe_workspace_size(int T, int top_k, int E_local, int H, int I, int mode);
 
 /* a1 -- routing (page 1 "Serving call chain": sigmoid + correction bias +
  * top-k + renormalise; "Key sources" routing row: the bias only selects, the
@@ -96,7 +116,9 @@ size_t moe_workspace_size(int T, int top_k, int E_local, int H, int I);
  *   slots ordered by key descending; w_k = s_k / sum_j s_j (double) times
  *   routed_scaling, rounded to float.
  *   topk_idx int32 [T, top_k] global expert ids; topk_w float [T, top_k].
- *   Logits must be finite. */
+ *   A NaN logit (or bias) gives a NaN key, which ranks below every other key
+ *   (NaN experts are chosen last, lower index first); if one is chosen, the
+ *   token's weights are NaN. */
 moe_status_t moe_route(const float* logits, int64_t ld_logits, const float* bias,
                        int T, int E, int top_k, float routed_scaling,
                        int32_t* topk_idx, float* topk_w, hipStream_t stream);
@@ -191,25 +213,31 @@ moe_status_t moe_fc1_situ(const uint8_t* xq, const uint8_t* xs, int T, int H, in
                           hipStream_t stream);
 
 /* a7 + a8 -- FC2 grouped GEMM and top-k combine (page 1 "Serving call chain":
- * GEMM2 then finalize; "Phase 2": non-fused finalize for bitwise determinism;
- * page 5: w2 [E, H, I/2], scales [E, H, I/32]).
+ * GEMM2 then finalize; "Phase 2": the non-fused finalize for bitwise
+ * determinism, next to the fused atomic one; page 5: w2 [E, H, I/2], scales
+ * [E, H, I/32]).
  *   hq, hs          from moe_fc1_situ.
- *   route_row       from moe_permute; topk_w from moe_route (float [T, top_k]).
+ *   expert_offsets, sorted_route, route_row   from moe_permute.
+ *   topk_w          from moe_route (float [T, top_k]).
  *   w2, w2_s        uint8 [E_local, H, I/2], [E_local, H, I/32].
+ *   mode            a moe_combine_t value (else MOE_ERR_ENUM).
  *   out             bf16 bits [T, H], row stride ld_out (>= H, multiple of 8):
- *                   out[t] = bf16_rne( sum over kept k, in k order, of
- *                   topk_w[t,k] * y[route_row[t,k]] ) with float accumulation;
- *                   a token with no kept slot gets zeros.  Bitwise
- *                   deterministic.
- *   workspace       the buffer moe_permute filled (holds the per-route FC2 rows
- *                   y [T*top_k, H] as fp16 of y / 2^e with one exponent e per
- *                   64 columns: 2^-11 relative, below the output's bf16 step). */
+ *                   out[t] = bf16_rne( sum over kept k of
+ *                   topk_w[t,k] * y[route_row[t,k]] ) with float accumulation
+ *                   (DETERMINISTIC: in k order, bitwise repeatable; ATOMIC: in
+ *                   the order the atomic adds land); a token with no kept slot
+ *                   gets zeros.
+ *   workspace       the buffer moe_permute filled, of at least
+ *                   moe_workspace_size(..., mode) bytes (DETERMINISTIC: holds
+ *                   the per-route FC2 rows y [T*top_k, H] as fp16 of y / 2^e
+ *                   with one exponent e per 64 columns, 2^-11 relative, below
+ *                   the output's bf16 step; ATOMIC: the float [T, H] sums). */
 moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                              int top_k, int E_local, const int32_t* expert_offsets,
-                             const int32_t* route_row, const float* topk_w,
-                             const uint8_t* w2, const uint8_t* w2_s, uint16_t* out,
-                             int64_t ld_out, void* workspace, size_t ws_bytes,
-                             hipStream_t stream);
+                             const int32_t* sorted_route, const int32_t* route_row,
+                             const float* topk_w, const uint8_t* w2, const uint8_t* w2_s,
+                             int mode, uint16_t* out, int64_t ld_out, void* workspace,
+                             size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Tiled weight layout (optional, one-time).  The calls above read the
@@ -252,7 +280,7 @@ typedef enum moe_w13_layout {
 } moe_w13_layout_t;
 
 /* moe_prepack_w13 for a w13 / w13_s whose rows are in `layout` order (a
- * moe_w13_layout_t value; anything else is MOE_ERR_SHAPE).  The tiled result
+ * moe_w13_layout_t value; anything else is MOE_ERR_ENUM).  The tiled result
  * is the same bytes moe_prepack_w13 gives for the [gate; up] reordering of
  * the input, so moe_fc1_situ_tiled computes the same layer for every layout.
  * (The checkpoint-layout moe_fc1_situ reads [gate; up] only.) */
@@ -275,8 +303,9 @@ moe_status_t moe_fc1_situ_tiled(const uint8_t* xq, const uint8_t* xs, int T, int
 /* moe_fc2_combine on tiled w2 (from moe_prepack_w2); same results. */
 moe_status_t moe_fc2_combine_tiled(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                                    int top_k, int E_local, const int32_t* expert_offsets,
-                                   const int32_t* route_row, const float* topk_w,
-                                   const uint8_t* w2t, const uint8_t* w2t_s, uint16_t* out,
+                                   const int32_t* sorted_route, const int32_t* route_row,
+                                   const float* topk_w, const uint8_t* w2t,
+                                   const uint8_t* w2t_s, int mode, uint16_t* out,
                                    int64_t ld_out, void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
 

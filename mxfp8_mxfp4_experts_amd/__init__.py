@@ -6,6 +6,8 @@ The layer is five C calls into ``libmi355moe.so`` (declared in
 quantisation and grouping as the one call ``moe_route_quant_permute``).
 """
 from ._binding import (  # noqa: F401
+    COMBINE_ATOMIC,
+    COMBINE_DETERMINISTIC,
     EXPORTS,
     MoEError,
     lib,

@@ -18,7 +18,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi355moe.so")
 
 MOE_STATUS = {
-    0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN",
+    0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_ALIGN", 4: "MOE_ERR_ENUM",
     5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED_DEVICE",
     8: "MOE_ERR_SCRATCH_LIMIT",
 }
@@ -33,6 +33,8 @@ EXPORTS = (
 
 # moe_w13_layout_t values (row order of a w13 tensor)
 W13_GATE_UP, W13_UP_GATE, W13_INTERLEAVED = 0, 1, 2
+# moe_combine_t values (how moe_fc2_combine sums a token's top-k rows)
+COMBINE_DETERMINISTIC, COMBINE_ATOMIC = 0, 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -52,7 +54,7 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.moe_strerror.restype = ctypes.c_char_p
     lib.moe_strerror.argtypes = [_I]
     lib.moe_workspace_size.restype = _SZ
-    lib.moe_workspace_size.argtypes = [_I, _I, _I, _I, _I]
+    lib.moe_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.moe_route.restype = _I
     lib.moe_route.argtypes = [_P, _I64, _P, _I, _I, _I, _F, _P, _P, _P]
     lib.moe_quant_mxfp8.restype = _I
@@ -68,8 +70,8 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.moe_fc1_situ.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _F, _F, _P, _P, _P,
                                  _SZ, _P]
     lib.moe_fc2_combine.restype = _I
-    lib.moe_fc2_combine.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _P,
-                                    _SZ, _P]
+    lib.moe_fc2_combine.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I, _P,
+                                    _I64, _P, _SZ, _P]
     lib.moe_fc1_situ_tiled.restype = _I
     lib.moe_fc1_situ_tiled.argtypes = lib.moe_fc1_situ.argtypes
     lib.moe_fc2_combine_tiled.restype = _I
@@ -139,10 +141,11 @@ def moe_abi_version() -> int:
     return lib().moe_abi_version()
 
 
-def moe_workspace_size(T: int, top_k: int, E_local: int, H: int, I: int) -> int:
-    n = lib().moe_workspace_size(T, top_k, E_local, H, I)
+def moe_workspace_size(T: int, top_k: int, E_local: int, H: int, I: int,
+                       mode: int = COMBINE_DETERMINISTIC) -> int:
+    n = lib().moe_workspace_size(T, top_k, E_local, H, I, int(mode))
     if n == 0:
-        raise ValueError("invalid sizes for moe_workspace_size")
+        raise ValueError("invalid sizes or combine mode for moe_workspace_size")
     return n
 
 
@@ -315,10 +318,11 @@ def moe_fc1_situ(xq, xs, top_k, expert_offsets, sorted_route, w13, w13_s, worksp
     return hq, hs
 
 
-def moe_fc2_combine(hq, hs, T, top_k, expert_offsets, route_row, topk_w, w2, w2_s, workspace,
-                    out=None, tiled: bool = False):
+def moe_fc2_combine(hq, hs, T, top_k, expert_offsets, sorted_route, route_row, topk_w, w2, w2_s,
+                    workspace, out=None, tiled: bool = False, mode: int = COMBINE_DETERMINISTIC):
     """``tiled``: w2 / w2_s come from ``moe_prepack_w2`` (calls
-    moe_fc2_combine_tiled)."""
+    moe_fc2_combine_tiled).  ``mode``: COMBINE_DETERMINISTIC or
+    COMBINE_ATOMIC (the workspace must be sized for it)."""
     _need(hq, "hq", torch.uint8)
     R, I = hq.shape
     dev = hq.device
@@ -331,6 +335,7 @@ def moe_fc2_combine(hq, hs, T, top_k, expert_offsets, route_row, topk_w, w2, w2_
     _need(hs, "hs", torch.uint8, (R, I // 32), device=dev)
     _need(w2_s, "w2_s", torch.uint8, (E_local, H, I // 32), device=dev)
     _need(expert_offsets, "expert_offsets", torch.int32, (E_local + 1,), device=dev)
+    _need(sorted_route, "sorted_route", torch.int32, (R,), device=dev)
     _need(route_row, "route_row", torch.int32, (R,), device=dev)
     _need(topk_w, "topk_w", torch.float32, (T, top_k), device=dev)
     _need(workspace, "workspace", torch.uint8, device=dev)
@@ -342,15 +347,24 @@ def moe_fc2_combine(hq, hs, T, top_k, expert_offsets, route_row, topk_w, w2, w2_
     _need(ob, "out", torch.uint16, contiguous=False, device=dev)
     name = "moe_fc2_combine_tiled" if tiled else "moe_fc2_combine"
     _check(name, getattr(lib(), name)(
-        _ptr(hq), _ptr(hs), T, H, I, top_k, E_local, _ptr(expert_offsets), _ptr(route_row),
-        _ptr(topk_w), _ptr(w2), _ptr(w2_s), _ptr(ob), out.stride(0), _ptr(workspace),
-        workspace.numel(), _stream()))
+        _ptr(hq), _ptr(hs), T, H, I, top_k, E_local, _ptr(expert_offsets), _ptr(sorted_route),
+        _ptr(route_row), _ptr(topk_w), _ptr(w2), _ptr(w2_s), int(mode), _ptr(ob), out.stride(0),
+        _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 
-def _prepack(name, w, w_s, H, I):
+def _weight_pair(name, w, w_s):
+    """A checkpoint weight [E, N, K/2] and its scales [E, N, K/32]: shapes and
+    dtypes checked here, since the kernels read every byte they imply."""
     _need(w, name + " weights", torch.uint8)
-    _need(w_s, name + " scales", torch.uint8, device=w.device)
+    if w.dim() != 3 or w.shape[2] % 16 != 0:
+        raise ValueError(f"{name} weights must be [E, N, K/2] with K a multiple of 32")
+    E, N, half_k = w.shape
+    _need(w_s, name + " scales", torch.uint8, (E, N, 2 * half_k // 32), device=w.device)
+    return E, N, 2 * half_k
+
+
+def _prepack(name, w, w_s, H, I):
     tw = torch.empty_like(w)
     tws = torch.empty_like(w_s)
     _check(name, getattr(lib(), name)(_ptr(w), _ptr(w_s), w.shape[0], H, I, _ptr(tw), _ptr(tws),
@@ -359,25 +373,24 @@ def _prepack(name, w, w_s, H, I):
 
 
 def moe_prepack_w13(w13, w13_s):
-    """Checkpoint w13 [E, 2I, H/2] + scales -> tiled copies (same shapes)."""
-    E, twoI, half_h = w13.shape
-    return _prepack("moe_prepack_w13", w13, w13_s, 2 * half_h, twoI // 2)
+    """Checkpoint w13 [E, 2I, H/2] + scales [E, 2I, H/32] -> tiled copies
+    (same shapes)."""
+    E, twoI, H = _weight_pair("moe_prepack_w13", w13, w13_s)
+    return _prepack("moe_prepack_w13", w13, w13_s, H, twoI // 2)
 
 
 def moe_prepack_w13_layout(w13, w13_s, layout: int):
-    """w13 [E, 2I, H/2] + scales whose rows are in ``layout`` order
-    (W13_GATE_UP, W13_UP_GATE or W13_INTERLEAVED) -> tiled copies."""
-    _need(w13, "moe_prepack_w13_layout weights", torch.uint8)
-    _need(w13_s, "moe_prepack_w13_layout scales", torch.uint8, device=w13.device)
-    E, twoI, half_h = w13.shape
+    """w13 [E, 2I, H/2] + scales [E, 2I, H/32] whose rows are in ``layout``
+    order (W13_GATE_UP, W13_UP_GATE or W13_INTERLEAVED) -> tiled copies."""
+    E, twoI, H = _weight_pair("moe_prepack_w13_layout", w13, w13_s)
     tw, tws = torch.empty_like(w13), torch.empty_like(w13_s)
     _check("moe_prepack_w13_layout", lib().moe_prepack_w13_layout(
-        _ptr(w13), _ptr(w13_s), E, 2 * half_h, twoI // 2, int(layout), _ptr(tw), _ptr(tws),
-        _stream()))
+        _ptr(w13), _ptr(w13_s), E, H, twoI // 2, int(layout), _ptr(tw), _ptr(tws), _stream()))
     return tw, tws
 
 
 def moe_prepack_w2(w2, w2_s):
-    """Checkpoint w2 [E, H, I/2] + scales -> tiled copies (same shapes)."""
-    E, H, half_i = w2.shape
-    return _prepack("moe_prepack_w2", w2, w2_s, H, 2 * half_i)
+    """Checkpoint w2 [E, H, I/2] + scales [E, H, I/32] -> tiled copies (same
+    shapes)."""
+    E, H, I = _weight_pair("moe_prepack_w2", w2, w2_s)
+    return _prepack("moe_prepack_w2", w2, w2_s, H, I)

@@ -2,6 +2,8 @@
 
 Run ``python -m mxfp8_mxfp4_experts_amd.build`` or call ``build()``.  Every
 source is compiled on each call (a cross-compile: no GPU is needed).
+``build_probes()`` also builds the test-only probe library
+(``tests/probe/libnumprobe.so``), which is never part of the layer.
 """
 from __future__ import annotations
 
@@ -41,13 +43,12 @@ def _run(cmd):
     return p.returncode, out
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def _build_so(sources, out_path, tag, verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = []
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        obj = os.path.join(BUILD_DIR, tag + "_" + os.path.basename(src) + ".o")
         rc, out = _run([HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj])
         return src, obj, rc, out
 
@@ -62,16 +63,33 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         objs.append(obj)
     if failed:
         raise RuntimeError("hipcc failed; see messages above")
-    tmp = OUT + ".tmp"
+    tmp = out_path + ".tmp"
     rc, out = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     if rc != 0:
         print(out, file=sys.stderr)
         raise RuntimeError("link failed")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out_path)
     if verbose:
-        print(f"[build] wrote {OUT}")
-    return OUT
+        print(f"[build] wrote {out_path}")
+    return out_path
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """The layer library ``libmi355moe.so`` from every source in csrc/."""
+    return _build_so(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), OUT, "lib", verbose, jobs)
+
+
+PROBE_DIR = os.path.join(ROOT, "tests", "probe")
+PROBE_OUT = os.path.join(PROBE_DIR, "libnumprobe.so")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """The test-only probe library (device functions of the FC kernels run
+    on inputs the GPU tests choose)."""
+    return _build_so([os.path.join(PROBE_DIR, "numerics_probe.hip")], PROBE_OUT, "probe",
+                     verbose)
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_probes(verbose=True)

@@ -68,6 +68,7 @@ const char* moe_strerror(int status) {
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size or stride is out of range";
     case MOE_ERR_ALIGN: return "a pointer or stride is misaligned";
+    case MOE_ERR_ENUM: return "an enum argument has no defined value";
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case MOE_ERR_UNSUPPORTED_DEVICE: return "current device is not gfx950";
@@ -77,9 +78,10 @@ const char* moe_strerror(int status) {
   }
 }
 
-size_t moe_workspace_size(int T, int top_k, int E_local, int H, int I) {
+size_t moe_workspace_size(int T, int top_k, int E_local, int H, int I, int mode) {
   if (!valid_hi(H, I) || !valid_window(top_k, E_local) || !valid_rows(T, top_k, H, I)) return 0;
-  return ws_layout(T, top_k, E_local, H, I).total;
+  if (mode != MOE_COMBINE_DETERMINISTIC && mode != MOE_COMBINE_ATOMIC) return 0;
+  return ws_layout(T, top_k, E_local, H, I, mode == MOE_COMBINE_ATOMIC).total;
 }
 
 moe_status_t moe_route(const float* logits, int64_t ld_logits, const float* bias, int T, int E,
@@ -232,21 +234,26 @@ moe_status_t moe_fc1_situ_tiled(const uint8_t* xq, const uint8_t* xs, int T, int
 
 static moe_status_t fc2_impl(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                              int top_k, int E_local, const int32_t* expert_offsets,
-                             const int32_t* route_row, const float* topk_w, const uint8_t* w2,
-                             const uint8_t* w2_s, uint16_t* out, int64_t ld_out,
-                             void* workspace, size_t ws_bytes, hipStream_t stream, bool tiled) {
+                             const int32_t* sorted_route, const int32_t* route_row,
+                             const float* topk_w, const uint8_t* w2, const uint8_t* w2_s, int mode,
+                             uint16_t* out, int64_t ld_out, void* workspace, size_t ws_bytes,
+                             hipStream_t stream, bool tiled) {
   if (!valid_hi(H, I) || !valid_window(top_k, E_local) || !valid_rows(T, top_k, H, I) ||
       ld_out < H || (tiled && H % 512 != 0))
     return MOE_ERR_SHAPE;
+  if (mode != MOE_COMBINE_DETERMINISTIC && mode != MOE_COMBINE_ATOMIC) return MOE_ERR_ENUM;
+  const bool atomic = mode == MOE_COMBINE_ATOMIC;
   if (!expert_offsets || !w2 || !w2_s || !workspace) return MOE_ERR_NULL;
-  if (T > 0 && (!hq || !hs || !route_row || !topk_w || !out)) return MOE_ERR_NULL;
+  if (T > 0 && (!hq || !hs || !route_row || !topk_w || !out || (atomic && !sorted_route)))
+    return MOE_ERR_NULL;
   if (!aligned(w2, 16) || !aligned(w2_s, 16) || !aligned(expert_offsets, 4) ||
       !aligned(workspace, 256))
     return MOE_ERR_ALIGN;
   if (T > 0 && (!aligned(hq, 16) || !aligned(hs, 16) || !aligned(route_row, 4) ||
-                !aligned(topk_w, 4) || !aligned(out, 16) || ld_out % 8 != 0))
+                !aligned(topk_w, 4) || !aligned(out, 16) || ld_out % 8 != 0 ||
+                (sorted_route && !aligned(sorted_route, 4))))
     return MOE_ERR_ALIGN;
-  WsLayout l = ws_layout(T, top_k, E_local, H, I);
+  WsLayout l = ws_layout(T, top_k, E_local, H, I, atomic);
   if (ws_bytes < l.total) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
   int n_cu = 0;
@@ -254,40 +261,51 @@ static moe_status_t fc2_impl(const uint8_t* hq, const uint8_t* hs, int T, int H,
   if (s != MOE_OK) return s;
   char* ws = static_cast<char*>(workspace);
   const int32_t* prefix = reinterpret_cast<const int32_t*>(ws + l.tile_prefix);
-  uint16_t* y = reinterpret_cast<uint16_t*>(ws + l.y);
-  int8_t* ye = reinterpret_cast<int8_t*>(ws + l.ye);
   uint32_t* act_st = reinterpret_cast<uint32_t*>(ws + l.act_st);
   int32_t* sched = reinterpret_cast<int32_t*>(ws + l.fc_sched);
-  hipError_t e = launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, ye,
-                            prefix, act_st, sched, n_cu, tiled, stream);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (atomic) {
+    float* acc = reinterpret_cast<float*>(ws + l.y);
+    if (launch_acc_clear(acc, T, H, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, nullptr, nullptr,
+                   sorted_route, topk_w, acc, prefix, act_st, sched, n_cu, tiled,
+                   stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    return finish(launch_acc_to_bf16(acc, T, H, out, ld_out, stream));
+  }
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + l.y);
+  int8_t* ye = reinterpret_cast<int8_t*>(ws + l.ye);
+  if (launch_fc2(hq, hs, T, H, I, top_k, E_local, expert_offsets, w2, w2_s, y, ye, nullptr,
+                 nullptr, nullptr, prefix, act_st, sched, n_cu, tiled, stream) != hipSuccess)
+    return MOE_ERR_HIP;
   return finish(launch_combine(y, ye, H, route_row, topk_w, T, top_k, out, ld_out, stream));
 }
 
 moe_status_t moe_fc2_combine(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                              int top_k, int E_local, const int32_t* expert_offsets,
-                             const int32_t* route_row, const float* topk_w, const uint8_t* w2,
-                             const uint8_t* w2_s, uint16_t* out, int64_t ld_out,
-                             void* workspace, size_t ws_bytes, hipStream_t stream) {
-  return fc2_impl(hq, hs, T, H, I, top_k, E_local, expert_offsets, route_row, topk_w, w2, w2_s,
-                  out, ld_out, workspace, ws_bytes, stream, false);
+                             const int32_t* sorted_route, const int32_t* route_row,
+                             const float* topk_w, const uint8_t* w2, const uint8_t* w2_s,
+                             int mode, uint16_t* out, int64_t ld_out, void* workspace,
+                             size_t ws_bytes, hipStream_t stream) {
+  return fc2_impl(hq, hs, T, H, I, top_k, E_local, expert_offsets, sorted_route, route_row,
+                  topk_w, w2, w2_s, mode, out, ld_out, workspace, ws_bytes, stream, false);
 }
 
 moe_status_t moe_fc2_combine_tiled(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
                                    int top_k, int E_local, const int32_t* expert_offsets,
-                                   const int32_t* route_row, const float* topk_w,
-                                   const uint8_t* w2t, const uint8_t* w2t_s, uint16_t* out,
+                                   const int32_t* sorted_route, const int32_t* route_row,
+                                   const float* topk_w, const uint8_t* w2t,
+                                   const uint8_t* w2t_s, int mode, uint16_t* out,
                                    int64_t ld_out, void* workspace, size_t ws_bytes,
                                    hipStream_t stream) {
-  return fc2_impl(hq, hs, T, H, I, top_k, E_local, expert_offsets, route_row, topk_w, w2t, w2t_s,
-                  out, ld_out, workspace, ws_bytes, stream, true);
+  return fc2_impl(hq, hs, T, H, I, top_k, E_local, expert_offsets, sorted_route, route_row,
+                  topk_w, w2t, w2t_s, mode, out, ld_out, workspace, ws_bytes, stream, true);
 }
 
 static moe_status_t prepack_impl(bool fc1, const uint8_t* w, const uint8_t* ws, int E_local,
                                  int H, int I, int layout, uint8_t* tw, uint8_t* tws,
                                  hipStream_t stream) {
   if (!valid_hi(H, I) || E_local < 1 || E_local > kMaxExperts) return MOE_ERR_SHAPE;
-  if (layout < MOE_W13_GATE_UP || layout > MOE_W13_INTERLEAVED) return MOE_ERR_SHAPE;
+  if (layout < MOE_W13_GATE_UP || layout > MOE_W13_INTERLEAVED) return MOE_ERR_ENUM;
   if (fc1 ? (I % 256 != 0) : (H % 512 != 0)) return MOE_ERR_SHAPE;
   if (!w || !ws || !tw || !tws) return MOE_ERR_NULL;
   if (!aligned(w, 16) || !aligned(ws, 16) || !aligned(tw, 16) || !aligned(tws, 16))

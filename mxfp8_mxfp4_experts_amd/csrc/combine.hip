@@ -3,7 +3,9 @@
 // finalize).  out[t] = bf16 of the sum over kept slots k, in slot order, of
 // w[t,k] * y[route_row[t,k]], accumulated in float32; masked and dropped
 // slots contribute nothing, and a token with no kept slot gets zeros.  The
-// FC2 rows arrive as fp16 with a power-of-two scale per 64 columns.
+// FC2 rows arrive as fp16 with a power-of-two scale per 64 columns.  The
+// fused atomic finalize adds the weighted rows in the FC2 epilogue instead
+// and only needs the clear and bf16 passes at the end of this file.
 #include "common.h"
 #include "fc_common.h"
 #include "launch.h"
@@ -76,7 +78,54 @@ __global__ __launch_bounds__(64) void combine_kernel(const uint16_t* __restrict_
   *reinterpret_cast<uint4*>(out + (size_t)t * ld_out + (size_t)c * 8) = o;
 }
 
+// Atomic combine, before FC2: the float [T, H] sums start at zero (a plain
+// store kernel, so the call chain stays capturable without memset nodes).
+// Each lane clears 4 floats; H is a multiple of 128.
+__global__ __launch_bounds__(256) void acc_clear_kernel(float4* __restrict__ acc, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) acc[i] = float4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Atomic combine, after FC2: out[t] = bf16_rne(acc[t]), 8 columns per lane.
+__global__ __launch_bounds__(256) void acc_to_bf16_kernel(const float* __restrict__ acc, int H,
+                                                          int64_t n8, uint16_t* __restrict__ out,
+                                                          int64_t ld_out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const int64_t per_row = H / 8;
+  const int64_t t = i / per_row, c = (i - t * per_row) * 8;
+  const float4 a = *reinterpret_cast<const float4*>(acc + t * H + c);
+  const float4 b = *reinterpret_cast<const float4*>(acc + t * H + c + 4);
+  uint4 o;
+  o.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
+  o.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
+  o.z = f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16);
+  o.w = f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16);
+  *reinterpret_cast<uint4*>(out + t * ld_out + c) = o;
+}
+
 }  // namespace
+
+hipError_t launch_acc_clear(float* acc, int T, int H, hipStream_t stream) {
+  const int64_t n4 = (int64_t)T * H / 4;
+  if (n4 <= 0) return hipSuccess;
+  const int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(acc_clear_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<float4*>(acc), n4);
+  return hipGetLastError();
+}
+
+hipError_t launch_acc_to_bf16(const float* acc, int T, int H, uint16_t* out, int64_t ld_out,
+                              hipStream_t stream) {
+  const int64_t n8 = (int64_t)T * H / 8;
+  if (n8 <= 0) return hipSuccess;
+  const int64_t blocks = (n8 + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(acc_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, acc, H, n8,
+                     out, ld_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const uint16_t* y, const int8_t* ye, int H, const int32_t* route_row,
                           const float* topk_w, int T, int K, uint16_t* out, int64_t ld_out,

@@ -51,14 +51,16 @@ struct WsLayout {
                         // kernels, then their 9 item-range bounds
   size_t act_st;        // uint32 [max(H, I) / 128][T * top_k]: an FC input's scale dwords,
                         // stage-major in grouped-row order (prefill-shaped FC kernels)
-  size_t y;             // fp16 [T * top_k][H]  (FC2 rows before the combine, scaled)
-  size_t ye;            // int8 [T * top_k][H / 64]: power-of-two scale of each 64 columns
+  size_t y;             // deterministic combine: fp16 [T * top_k][H] (FC2 rows before the
+                        // combine, scaled); atomic combine: float [T][H] (the weighted sums)
+  size_t ye;            // deterministic combine: int8 [T * top_k][H / 64], the power-of-two
+                        // scale of each 64 columns (atomic combine: empty)
   size_t total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I) {
+inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I, bool atomic = false) {
   WsLayout l;
   size_t off = 0;
   l.tile_prefix = off;
@@ -71,9 +73,10 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I) {
   l.act_st = off;
   off = align256(off + (size_t)T * top_k * (size_t)((H > I ? H : I) / 32));
   l.y = off;
-  off = align256(off + sizeof(uint16_t) * (size_t)T * top_k * H);
+  off = atomic ? align256(off + sizeof(float) * (size_t)T * H)
+               : align256(off + sizeof(uint16_t) * (size_t)T * top_k * H);
   l.ye = off;
-  off = align256(off + (size_t)T * top_k * (H / 64));
+  off = atomic ? off : align256(off + (size_t)T * top_k * (H / 64));
   l.total = off;
   return l;
 }

@@ -40,10 +40,7 @@ namespace {
 // 128-K slices per super-step: the operands of two super-steps are in
 // registers at a time (about 120 VGPRs for two slices), which leaves room for
 // two wavefronts per SIMD.
-#ifndef DECODE_SJ
-#define DECODE_SJ 2
-#endif
-constexpr int kSJ = DECODE_SJ;
+constexpr int kSJ = 2;
 
 // Tile list of the decode-shaped kernel: 32-row tiles (tile prefix 0), whose
 // tile -> expert map the grouping step writes after the prefixes.
@@ -359,7 +356,8 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
 
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      uint16_t* y, int8_t* ye, const int32_t* tile_prefix_all,
+                      uint16_t* y, int8_t* ye, const int32_t* sorted_route,
+                      const float* topk_w, float* out_acc, const int32_t* tile_prefix_all,
                       uint32_t* act_st, int32_t* sched, int n_cu, bool tiled,
                       hipStream_t stream) {
   FcParams p{};
@@ -369,6 +367,7 @@ hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I,
   p.expert_offsets = offs; p.E_local = E_local;
   p.n_units = H / 64;
   p.y = y; p.ye = ye;
+  p.combine_route = sorted_route; p.topk_w = topk_w; p.out_acc = out_acc;
   return launch_fc<false>(p, T * top_k, tile_prefix_all, n_cu, tiled, stream);
 }
 

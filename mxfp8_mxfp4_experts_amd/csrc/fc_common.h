@@ -38,41 +38,70 @@ struct FcParams {
   float alpha, beta;
   uint8_t* hq;               // FC1 out [R, I]
   uint8_t* hs;               // FC1 out [R, I/32]
-  uint16_t* y;               // FC2 out [R, N]: fp16 of y / 2^ye
+  uint16_t* y;               // FC2 out [R, N]: fp16 of y / 2^ye (deterministic combine)
   int8_t* ye;                // FC2 out [R, N / 64]: scale exponent per 64 columns
+  // Atomic combine (FC2 only; out_acc == nullptr otherwise): grouped row r
+  // adds topk_w[route] * y[r] into out_acc[route / top_k] with
+  // route = combine_route[r].
+  const int32_t* combine_route;
+  const float* topk_w;
+  float* out_acc;            // [T, N] float sums
 };
 
 // SiTU(g, u) = alpha tanh(g / alpha) sigmoid(g) * beta tanh(u / beta)
 // (page 1, "真实 checkpoint 契约": the SiTU activation with alpha = 4, beta =
-// 25; alpha, beta > 0), from three hardware base-2 exponentials and one
-// reciprocal.  With z1 = e^(-2g/alpha), z2 = e^(-g), w = e^(-2u/beta):
+// 25; alpha, beta > 0), in float32 from hardware base-2 exponentials and
+// reciprocals.  With z1 = e^(-2g/alpha), z2 = e^(-g), w = e^(-2u/beta):
 //   tanh(g/alpha) = (1 - z1) / (1 + z1),  sigmoid(g) = 1 / (1 + z2),
-//   tanh(u/beta) = (1 - w) / (1 + w),
-// so SiTU = alpha beta (1 - z1)(1 - w) / ((1 + z1)(1 + z2)(1 + w)).  The
-// numerators take the sign of g and u (tanh keeps the sign of zero).  Each
-// exponent is capped at e^40: the numerator stays finite, and where the
-// denominator overflows the true value is below 1e-16 and the result is a
-// signed zero.  Accuracy: a few float32 ulps relative, ~1e-7 absolute near
-// zero, far inside the E4M3 step the result goes through next.  A NaN input
-// gives 0 here (the requantisation rule sends NaN to code 0 and leaves it
-// out of the block maximum, which is what 0 does).
+//   tanh(u/beta) = (1 - w) / (1 + w).
+// 1 - z cancels when its argument y = g/alpha or u/beta is small (u/beta
+// nearly always is: |u| is a few units against beta = 25), so for |y| <= 3/8
+// tanh(y) comes from its Taylor series through y^11 instead (the first
+// omitted term, 21844/6081075 y^13, is below 2^-25 |y| there), with a
+// denominator of 1.  The numerators keep the signs of g and u (tanh keeps the
+// sign of zero).  z1 and w are capped at e^40, where both tanh quotients are
+// already +-1 in float32, so the two tanh factors and their product stay
+// finite; the sigmoid takes its own reciprocal of 1 + z2, which is 0 once z2
+// overflows (g < -88: the true value is below 1e-36).  Accuracy: a few
+// float32 ulps relative plus the rounding of the exponent g log2(e) (about
+// |g| 2^-24 relative).  A NaN input gives 0 here (the requantisation rule
+// sends NaN to code 0 and leaves it out of the block maximum, which is what
+// 0 does).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 struct SituConst {
   float k1, k2, k3, ab;   // -2 log2(e) / alpha, -log2(e), -2 log2(e) / beta, alpha beta
+  float ia, ib;           // 1 / alpha, 1 / beta
 };
 __device__ __forceinline__ SituConst situ_const(float alpha, float beta) {
   const float l2e = 1.4426950408889634f;
-  return SituConst{-2.0f * l2e / alpha, -l2e, -2.0f * l2e / beta, alpha * beta};
+  return SituConst{-2.0f * l2e / alpha, -l2e, -2.0f * l2e / beta, alpha * beta,
+                   1.0f / alpha, 1.0f / beta};
+}
+// tanh(y) for |y| <= 3/8: y + y^3 (-1/3 + y^2 (2/15 + y^2 (-17/315 +
+// y^2 (62/2835 + y^2 (-1382/155925))))), sign of zero kept.
+__device__ __forceinline__ float tanh_series(float y) {
+  const float y2 = y * y;
+  float p = -1382.0f / 155925.0f;
+  p = fmaf(p, y2, 62.0f / 2835.0f);
+  p = fmaf(p, y2, -17.0f / 315.0f);
+  p = fmaf(p, y2, 2.0f / 15.0f);
+  p = fmaf(p, y2, -1.0f / 3.0f);
+  return copysignf(fmaf(p * y2, y, y), y);
 }
 __device__ __forceinline__ float situ(float g, float u, const SituConst& c) {
   const float cap = 57.70780163555853f;   // 40 log2(e)
   const float z1 = fast_exp2(fminf(g * c.k1, cap));
-  const float z2 = fast_exp2(fminf(g * c.k2, cap));
+  const float z2 = fast_exp2(g * c.k2);
   const float w = fast_exp2(fminf(u * c.k3, cap));
-  const float num = copysignf(1.0f - z1, g) * copysignf(1.0f - w, u);
-  const float den = (1.0f + z1) * (1.0f + z2) * (1.0f + w);
-  const float v = c.ab * num * fast_rcp(den);
+  const float y1 = g * c.ia, y2 = u * c.ib;
+  const bool s1 = fabsf(y1) <= 0.375f, s2 = fabsf(y2) <= 0.375f;
+  const float n1 = s1 ? tanh_series(y1) : copysignf(1.0f - z1, g);
+  const float n2 = s2 ? tanh_series(y2) : copysignf(1.0f - w, u);
+  const float d1 = s1 ? 1.0f : 1.0f + z1;
+  const float d2 = s2 ? 1.0f : 1.0f + w;
+  const float t = c.ab * (n1 * n2) * fast_rcp(d1 * d2);
+  const float v = t * fast_rcp(1.0f + z2);
   return __builtin_isunordered(g, u) ? 0.0f : v;
 }
 // Four E4M3 codes of x / s (s a normal power of two, |x / s| <= 448), packed
@@ -108,7 +137,9 @@ __device__ __forceinline__ void pin_acc_agpr(v4f (&acc)[4]) {
 // FC1: blocks 0/1 are gate columns [c0, c0+32), blocks 2/3 the matching up
 // columns; SiTU, the 32-column absmax (two lane-xor steps over the lane
 // groups), the E8M0 exponent and the E4M3 codes are all computed here.
-// FC2: the float rows go to y.  Every lane must call this (shuffles).
+// FC2: the float rows go to y, or with the atomic combine are added, times
+// the route's weight, into the token's float sums.  Every lane must call this
+// (shuffles).
 template <bool FC1>
 __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc)[4], int row,
                                               bool valid, int u, int g) {
@@ -150,6 +181,19 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
       *reinterpret_cast<uint32_t*>(dst) = q0;
       *reinterpret_cast<uint32_t*>(dst + 16) = q1;
       if (g == 0) p.hs[(size_t)row * (p.I / 32) + c0 / 32] = (uint8_t)(ex + 127);
+    }
+  } else if (p.out_acc != nullptr) {
+    // Atomic combine: this lane's 16 columns of grouped row `row` (columns
+    // u 64 + 16 bk + 4 g + r), weighted, into its token's sums.  The adds
+    // land in no fixed order, so the sums' rounding varies from run to run.
+    if (valid) {
+      const int route = p.combine_route[row];
+      const float w = p.topk_w[route];
+      float* dst = p.out_acc + (size_t)(route / p.top_k) * p.N + u * 64 + 4 * g;
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + 16 * bk + r, w * acc[bk][r]);
     }
   } else {
     // The 64 columns of the unit for this row (16 values in each of the four

@@ -29,9 +29,13 @@ hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I,
                       uint8_t* hq, uint8_t* hs, const int32_t* tile_prefix_all,
                       uint32_t* act_st, int32_t* sched, int n_cu, bool tiled,
                       hipStream_t stream);
+// FC2 rows into y / ye (deterministic combine), or, with out_acc set, the
+// atomic combine: each grouped row r adds topk_w[route] times its row into
+// out_acc [T, H] (route = sorted_route[r]).
 hipError_t launch_fc2(const uint8_t* hq, const uint8_t* hs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const uint8_t* w2, const uint8_t* w2_s,
-                      uint16_t* y, int8_t* ye, const int32_t* tile_prefix_all,
+                      uint16_t* y, int8_t* ye, const int32_t* sorted_route,
+                      const float* topk_w, float* out_acc, const int32_t* tile_prefix_all,
                       uint32_t* act_st, int32_t* sched, int n_cu, bool tiled,
                       hipStream_t stream);
 struct FcParams;
@@ -50,5 +54,10 @@ hipError_t launch_prepack(bool fc1, const uint8_t* w, const uint8_t* ws, int E_l
 hipError_t launch_combine(const uint16_t* y, const int8_t* ye, int H, const int32_t* route_row,
                           const float* topk_w, int T, int K, uint16_t* out, int64_t ld_out,
                           hipStream_t stream);
+// Atomic combine: clear the float [T, H] sums before FC2; round them to bf16
+// after it.
+hipError_t launch_acc_clear(float* acc, int T, int H, hipStream_t stream);
+hipError_t launch_acc_to_bf16(const float* acc, int T, int H, uint16_t* out, int64_t ld_out,
+                              hipStream_t stream);
 
 }  // namespace mi355moe

@@ -10,8 +10,13 @@
 
 namespace mi355moe {
 
+// Order-preserving unsigned image of a float selection key: larger keys map
+// to larger values, -inf to 0x007FFFFF.  A NaN key (a NaN logit or bias)
+// maps to 1, below every other key, so NaN experts rank last and among
+// themselves by lower index (a stable descending sort puts NaN last too).
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 1u;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 

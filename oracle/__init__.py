@@ -17,13 +17,15 @@ Pinning status (what each function is checked against, in
 
 * codecs: OCP MX closed forms (E4M3 extremes, E2M1 magnitudes), torch's
   independent float8_e4m3fn / float8_e8m0fnu conversions, exhaustive
-  brute-force nearest-value search over every bf16 pattern;
+  brute-force nearest-value search over every bf16 pattern; the report-only
+  bf16 rounding against torch's bfloat16 conversion and exact rationals;
 * route: brute-force sort, the bias-free special case (top-k of the logits),
   constructed ties, weight invariants;
 * permute: brute-force per-expert scan;
 * FC1 / FC2 / layer: independent per-token brute force (``oracle.brute``),
   one-hot layout probes (nibble order, gate/up halves, scale indexing),
-  integer special cases;
+  integer special cases; the report-only accumulators and |product| sums
+  against each other and the triangle inequality;
 * SiTU: limits and identities of the closed form;
 * combine / expert-parallel masking: linearity and the shard-sum invariant.
 

@@ -122,7 +122,8 @@ def situ(g, u, alpha: float = 4.0, beta: float = 25.0):
 # a4 + a5 + a6: FC1, SiTU, requantisation
 # --------------------------------------------------------------------------
 def fc1_situ_requant(xq, xs, expert_offsets, sorted_route, top_k, w13, w13_s,
-                     alpha=4.0, beta=25.0, return_acc=False, return_pre=False):
+                     alpha=4.0, beta=25.0, return_acc=False, return_pre=False,
+                     return_absum=False):
     """Per local expert: gather its routed rows of the MXFP8 activations,
     multiply by the dequantised MXFP4 w13 (exact in float64), split the
     result into the gate half (columns < I) and the up half (columns >= I),
@@ -136,7 +137,10 @@ def fc1_situ_requant(xq, xs, expert_offsets, sorted_route, top_k, w13, w13_s,
     rounded before it.  Rows are in grouped order.
     Returns (hq uint8 [n_kept, I], hs uint8 [n_kept, I/32]) and, with
     ``return_acc``, the float64 FC1 accumulators [n_kept, 2I]; with
-    ``return_pre``, the float64 SiTU output before requantisation.
+    ``return_pre``, the float64 SiTU output before requantisation; with
+    ``return_absum``, the sums of |products| behind each accumulator,
+    |A| @ |W|^T [n_kept, 2I] (report only: the scale of an accumulation
+    error, used to judge a requantised byte that differs).
     """
     w13 = np.asarray(w13)
     E_local, twoI, _ = w13.shape
@@ -144,6 +148,7 @@ def fc1_situ_requant(xq, xs, expert_offsets, sorted_route, top_k, w13, w13_s,
     n_kept = int(expert_offsets[-1])
     a_all = np.empty((n_kept, I), np.float64)
     acc_all = np.empty((n_kept, twoI), np.float64) if return_acc else None
+    abs_all = np.empty((n_kept, twoI), np.float64) if return_absum else None
     for e in range(E_local):
         r0, r1 = int(expert_offsets[e]), int(expert_offsets[e + 1])
         if r1 == r0:
@@ -154,9 +159,12 @@ def fc1_situ_requant(xq, xs, expert_offsets, sorted_route, top_k, w13, w13_s,
         acc = A @ W.T
         if return_acc:
             acc_all[r0:r1] = acc
+        if return_absum:
+            abs_all[r0:r1] = np.abs(A) @ np.abs(W).T
         a_all[r0:r1] = situ(acc[:, :I], acc[:, I:], alpha, beta)
     hq, hs = mxfp8_quantize(a_all) if n_kept else (np.zeros((0, I), np.uint8), np.zeros((0, I // 32), np.uint8))
-    extra = ([acc_all] if return_acc else []) + ([a_all] if return_pre else [])
+    extra = (([acc_all] if return_acc else []) + ([a_all] if return_pre else [])
+             + ([abs_all] if return_absum else []))
     return (hq, hs, *extra) if extra else (hq, hs)
 
 
@@ -206,11 +214,13 @@ def combine(y, route_row, topk_w, T: int, top_k: int):
 # --------------------------------------------------------------------------
 def oracle_layer(x_bf16, logits, bias, w13, w13_s, w2, w2_s, *, top_k,
                  expert_offset=0, routed_scaling=1.0, alpha=4.0, beta=25.0,
-                 topk_idx=None, topk_w=None):
+                 topk_idx=None, topk_w=None, report=False):
     """All steps a1..a8; returns a dict of every intermediate.
 
     ``topk_idx``/``topk_w`` may be given to bypass routing (masked-slot
-    cases); weights are indexed by local expert."""
+    cases); weights are indexed by local expert.  With ``report`` the dict
+    also holds the FC1 accumulators ``acc`` and their sums of |products|
+    ``absum`` (report only)."""
     x_bf16 = np.asarray(x_bf16)
     T = x_bf16.shape[0]
     w13 = np.asarray(w13)
@@ -219,12 +229,17 @@ def oracle_layer(x_bf16, logits, bias, w13, w13_s, w2, w2_s, *, top_k,
         topk_idx, topk_w = route(logits, bias, top_k, routed_scaling)
     xq, xs = quant_x(x_bf16)
     offs, sroute, rrow = permute(topk_idx, expert_offset, E_local)
-    hq, hs, a = fc1_situ_requant(xq, xs, offs, sroute, top_k, w13, w13_s, alpha, beta,
-                                 return_pre=True)
+    fc1 = fc1_situ_requant(xq, xs, offs, sroute, top_k, w13, w13_s, alpha, beta,
+                           return_acc=report, return_pre=True, return_absum=report)
+    hq, hs = fc1[0], fc1[1]
+    a = fc1[3] if report else fc1[2]
     y = fc2(hq, hs, offs, w2, w2_s)
     out = combine(y, rrow, topk_w, T, top_k)
-    return dict(topk_idx=topk_idx, topk_w=topk_w, xq=xq, xs=xs, expert_offsets=offs,
-                sorted_route=sroute, route_row=rrow, hq=hq, hs=hs, a=a, y=y, out=out)
+    res = dict(topk_idx=topk_idx, topk_w=topk_w, xq=xq, xs=xs, expert_offsets=offs,
+               sorted_route=sroute, route_row=rrow, hq=hq, hs=hs, a=a, y=y, out=out)
+    if report:
+        res.update(acc=fc1[2], absum=fc1[4])
+    return res
 
 
 def oracle_tokens(tokens, x_bf16, topk_idx, topk_w, weight_fn, *, top_k, expert_offset,
@@ -237,7 +252,8 @@ def oracle_tokens(tokens, x_bf16, topk_idx, topk_w, weight_fn, *, top_k, expert_
     the corresponding rows of ``oracle_layer``.  ``weight_fn(e_local)``
     returns (w13[e], w13_s[e], w2[e], w2_s[e]) as numpy arrays.
     Returns dict(out [n,H] float64, h {(j, k): (hq, hs, SiTU output before
-    requantisation)} for sampled token j and slot k).
+    requantisation, FC1 accumulators, their sums of |products|)} for sampled
+    token j and slot k; the last two are report only).
     """
     tokens = list(tokens)
     xq, xs = quant_x(np.asarray(x_bf16)[tokens])
@@ -258,6 +274,7 @@ def oracle_tokens(tokens, x_bf16, topk_idx, topk_w, weight_fn, *, top_k, expert_
         A = mxfp8_dequantize(xq[rows], xs[rows])
         W = mxfp4_dequantize(w13e, w13se)
         acc = A @ W.T
+        absum = np.abs(A) @ np.abs(W).T
         I = W.shape[0] // 2
         a = situ(acc[:, :I], acc[:, I:], alpha, beta)
         hq, hs = mxfp8_quantize(a)
@@ -265,7 +282,7 @@ def oracle_tokens(tokens, x_bf16, topk_idx, topk_w, weight_fn, *, top_k, expert_
         y = mxfp8_dequantize(hq, hs) @ W2.T
         for i, (j, k) in enumerate(need[e]):
             ys[(j, k)] = y[i]
-            hqs[(j, k)] = (hq[i], hs[i], a[i])
+            hqs[(j, k)] = (hq[i], hs[i], a[i], acc[i], absum[i])
     for j, t in enumerate(tokens):
         for k in range(top_k):
             if (j, k) in ys:

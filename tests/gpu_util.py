@@ -66,32 +66,54 @@ def assert_output_close(out, ref, tag=""):
     print(f"[{tag}] max|err|/RMS={st['max_err_over_rms']:.4g} cosine={st['cosine']:.8f} "
           f"bf16 floor={st['bf16_floor']:.4g}", flush=True)
     assert np.all(np.isfinite(out))
-    assert st["max_err_over_rms"] <= 2e-2, st
+    assert (st["max_err_over_rms"] if raw else beyond) <= 2e-2, st
     assert st["cosine"] >= 0.9995, st
     return st
 
 
-E4M3_POS = None
+# Bound on the block-scaled MFMA's accumulation error: one 16x16x128 MFMA
+# step adds at most ACC_EPS times the sum of |products| of its 128-K slice
+# (tests/test_gpu_numerics.py measures at most 8.9e-6, about 2^-16.8, for a
+# single step with the layer's value distributions; 2^-15 leaves a factor of
+# 3.4), so by the triangle inequality a dot product over K is off by at most
+# ACC_EPS times its whole sum of |products| (measured at K = 7168: 3.6e-7).
+ACC_EPS = 2.0 ** -15
 
 
-def _e4m3_grid():
-    global E4M3_POS
-    if E4M3_POS is None:
-        from oracle.codecs import E4M3_TABLE
-        E4M3_POS = E4M3_TABLE[:0x7F].copy()
-    return E4M3_POS
+def situ_error_bound(g, u, absum_g, absum_u, alpha=4.0, beta=25.0):
+    """Largest |SiTU_gpu - SiTU(g, u)| when the GPU's accumulators carry at
+    most ACC_EPS * absum of error and its float32 SiTU is within
+    (32 + 2|g|) 2^-24 relative (both measured in tests/test_gpu_numerics.py):
+    first-order terms with a 25% margin plus the second-order ones."""
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        tg, tu = np.tanh(g / alpha), np.tanh(u / beta)
+        sg = 1.0 / (1.0 + np.exp(-g))
+        gate, up = alpha * tg * sg, beta * tu
+        dgate = (1.0 - tg * tg) * sg + alpha * tg * sg * (1.0 - sg)
+        dup = 1.0 - tu * tu
+        dg, du = ACC_EPS * np.asarray(absum_g), ACC_EPS * np.asarray(absum_u)
+        first = np.abs(dgate * up) * dg + np.abs(gate * dup) * du
+        second = 0.5 * (np.abs(up) * dg * dg + 0.1 * np.abs(gate) * du * du) + np.abs(dgate * dup) * dg * du
+        a = gate * up
+        bound = 1.25 * first + second + (32.0 + 2.0 * np.abs(g)) * 2.0 ** -24 * np.abs(a) + 1e-30
+    return np.where(np.isfinite(bound), bound, np.inf)
 
 
-def check_requant(hq_g, hs_g, a_ref, hq_ref, hs_ref, tag="", max_frac=1e-3, mid_tol=0.05):
+def check_requant(hq_g, hs_g, hq_ref, hs_ref, a_ref, acc_ref, absum_ref, tag="", max_frac=5e-3,
+                  alpha=4.0, beta=25.0):
     """The GPU requantises float32 accumulators, the oracle exact float64 ones,
     so a byte may differ where the exact value sits next to an E4M3 rounding
-    point.  Each differing element must be the E4M3 rounding of some value
-    within ``mid_tol`` of the exact one (in units of the scaled element, whose
-    range is [0, 448]; the float32 error of the GPU's SiTU output is about
-    1e-4 there): |v - y| <= |rne(y) - y| + 2 * mid_tol.  A differing scale
-    must keep the group's absmax within (224, 448] up to 1e-3.  Returns the
+    point or a scale boundary.  Every byte is held to what the GPU's measured
+    error allows: with da = situ_error_bound(...) for each element,
+      * the GPU's scale exponent lies between the rule's exponents for the
+        group absmax minus and plus max(da) over the group;
+      * the GPU's element code lies between the nearest-even codes of
+        (a - da) / 2^e and (a + da) / 2^e at the GPU's exponent e.
+    At most ``max_frac`` of the bytes of the rows may differ.  Returns the
     differing dequantised amounts, float64 [rows, I]."""
-    from oracle.codecs import e4m3_decode, e4m3_encode, mxfp8_dequantize
+    from oracle.codecs import e4m3_decode, e4m3_encode, mx_exponent, mxfp8_dequantize
 
     hq_g, hs_g = np.asarray(hq_g), np.asarray(hs_g)
     rows, I = hq_g.shape
@@ -99,32 +121,32 @@ def check_requant(hq_g, hs_g, a_ref, hq_ref, hs_ref, tag="", max_frac=1e-3, mid_
     frac_s = byte_mismatch(hs_g, hs_ref)
     print(f"[{tag}] hq mismatch {frac_q:.3g}, hs mismatch {frac_s:.3g}", flush=True)
     assert frac_q <= max_frac and frac_s <= max_frac, (frac_q, frac_s)
-    a = np.asarray(a_ref, np.float64).reshape(rows, I // 32, 32)
-    amax = np.abs(a).max(-1)
+    a = np.asarray(a_ref, np.float64).reshape(rows, I)
+    acc = np.asarray(acc_ref, np.float64).reshape(rows, 2 * I)
+    absum = np.asarray(absum_ref, np.float64).reshape(rows, 2 * I)
+    da = situ_error_bound(acc[:, :I], acc[:, I:], absum[:, :I], absum[:, I:], alpha, beta)
+    ag = np.where(np.isnan(a), 0.0, np.abs(a)).reshape(rows, I // 32, 32)
+    dag = da.reshape(rows, I // 32, 32).max(-1)
+    amax = ag.max(-1)
     eg = hs_g.astype(np.int64) - 127
-    bad_s = hs_g != hs_ref
-    if bad_s.any():
-        r = amax[bad_s] * np.ldexp(1.0, -eg[bad_s])
-        assert np.all((r > 224 * (1 - 1e-3)) & (r <= 448 * (1 + 1e-3))), "scale flip not at a boundary"
-    diff = (hq_g != hq_ref).reshape(rows, I // 32, 32) | bad_s[..., None]
+    e_lo = mx_exponent(np.maximum(amax - dag, 0.0), 448.0)
+    e_hi = mx_exponent(amax + dag, 448.0)
+    bad_s = (eg < e_lo) | (eg > e_hi)
+    assert not bad_s.any(), f"[{tag}] scale byte outside what the error bound allows"
+    diff = (hq_g != np.asarray(hq_ref)).reshape(rows, I // 32, 32) | (hs_g != hs_ref)[..., None]
     if diff.any():
-        y = (a * np.ldexp(1.0, -eg)[..., None])[diff]        # exact value at the GPU's scale
-        cg = hq_g.reshape(rows, I // 32, 32)[diff]
-        rne = e4m3_encode(y)
-        other = cg != rne                                     # not the correctly rounded code
-        if other.any():
-            # The GPU rounds a value y' with |y' - y| <= mid_tol to its nearest
-            # grid point v, so |v - y| <= |rne(y) - y| + 2 * mid_tol.
-            yo = y[other]
-            vg = e4m3_decode(cg[other])
-            vr = e4m3_decode(rne[other])
-            yc = np.clip(yo, -448.0, 448.0)
-            excess = np.abs(vg - yc) - np.abs(vr - yc)
-            worst = int(np.argmax(excess))
-            assert excess[worst] <= 2 * mid_tol, (
-                f"requantised byte {cg[other][worst]:#04x} for exact scaled value "
-                f"{yo[worst]!r} (nearest code {rne[other][worst]:#04x}) is "
-                f"{excess[worst]:.4g} farther than the nearest")
+        scale = np.ldexp(1.0, -eg)[..., None]
+        a3 = a.reshape(rows, I // 32, 32)
+        d3 = da.reshape(rows, I // 32, 32)
+        lo = e4m3_decode(e4m3_encode(((a3 - d3) * scale)[diff]))
+        hi = e4m3_decode(e4m3_encode(((a3 + d3) * scale)[diff]))
+        vg = e4m3_decode(hq_g.reshape(rows, I // 32, 32)[diff])
+        ok = (vg >= lo) & (vg <= hi) | ~np.isfinite(a3[diff])
+        if not ok.all():
+            i = int(np.argmin(ok))
+            raise AssertionError(
+                f"[{tag}] requantised value {vg[i]!r} outside [{lo[i]!r}, {hi[i]!r}] "
+                f"(exact scaled {(a3 * scale)[diff][i]!r})")
     return mxfp8_dequantize(hq_g, hs_g) - mxfp8_dequantize(hq_ref, hs_ref)
 
 
@@ -148,15 +170,23 @@ def flip_allowance(delta, tokens, K, route_row, topk_w, expert_of_row, w2_deq, H
     return out
 
 
-def assert_output_with_allowance(out, ref, allowance, tag=""):
+def assert_output_with_allowance(out, ref, allowance, tag="", raw=True):
+    """The output bar, max|out - ref| <= 2e-2 RMS(ref) and cosine >= 0.9995.
+
+    ``raw``: on the raw error (the named workloads).  Otherwise (small test
+    shapes, H <= 1024, where an output sums few terms and one E4M3 step of a
+    single FC2 input can move it by more than 2% of its RMS) on the error
+    beyond ``allowance``, the largest change the differing requantised bytes
+    can cause; check_requant has already held each of those bytes to the
+    measured hardware error.  Both figures are printed."""
     st = output_stats(out, ref)
     allow = 0.0 if allowance is None else allowance
     excess = np.abs(np.asarray(out, np.float64) - ref) - np.asarray(allow)
-    worst = float(excess.max()) / st["rms"] if st["rms"] > 0 else float(excess.max())
+    beyond = float(excess.max()) / st["rms"] if st["rms"] > 0 else float(excess.max())
     print(f"[{tag}] max|err|/RMS={st['max_err_over_rms']:.4g} (beyond the requant-flip bound "
-          f"{worst:.4g}) cosine={st['cosine']:.8f} bf16 floor={st['bf16_floor']:.4g}", flush=True)
+          f"{beyond:.4g}) cosine={st['cosine']:.8f} bf16 floor={st['bf16_floor']:.4g}", flush=True)
     assert np.all(np.isfinite(out))
-    assert worst <= 2e-2, st
+    assert (st["max_err_over_rms"] if raw else beyond) <= 2e-2, st
     assert st["cosine"] >= 0.9995, st
     return st
 

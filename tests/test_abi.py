@@ -40,21 +40,25 @@ def test_library_exports_every_header_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.moe_abi_version() == 1
-    for code in (0, 1, 2, 3, 5, 6, 7, 8):
+    assert lib.moe_abi_version() == 2
+    for code in (0, 1, 2, 3, 4, 5, 6, 7, 8):
         assert lib.moe_strerror(code)
     assert lib.moe_strerror(99) == b"unknown status"
 
 
 def test_workspace_size(lib):
-    n = lib.moe_workspace_size(8, 16, 896, 7168, 3584)
+    n = lib.moe_workspace_size(8, 16, 896, 7168, 3584, 0)
     # tile prefix + restaged scale dwords [T*K, max(H, I)/32] + y rows [T*K, H] fp16
     # + their scale exponents [T*K, H/64]
     R = 8 * 16
     assert n >= R * (7168 // 32) + R * 7168 * 2 + R * (7168 // 64) and n % 256 == 0
-    assert lib.moe_workspace_size(8, 16, 896, 7000, 3584) == 0      # H % 128
-    assert lib.moe_workspace_size(8, 0, 896, 7168, 3584) == 0       # top_k
-    assert lib.moe_workspace_size(8, 16, 5000, 7168, 3584) == 0     # E_local
+    # atomic combine: the float [T, H] sums instead of the per-route rows
+    na = lib.moe_workspace_size(8, 16, 896, 7168, 3584, 1)
+    assert na >= R * (7168 // 32) + 8 * 7168 * 4 and na % 256 == 0 and na < n
+    assert lib.moe_workspace_size(8, 16, 896, 7168, 3584, 2) == 0   # unknown mode
+    assert lib.moe_workspace_size(8, 16, 896, 7000, 3584, 0) == 0   # H % 128
+    assert lib.moe_workspace_size(8, 0, 896, 7168, 3584, 0) == 0    # top_k
+    assert lib.moe_workspace_size(8, 16, 5000, 7168, 3584, 0) == 0  # E_local
 
 
 FAKE = 1 << 20          # 16-byte aligned, never dereferenced by a failing call
@@ -121,8 +125,8 @@ def test_route_quant_permute_validation(lib):
 
 def test_prepack_layout_validation(lib):
     f = lib.moe_prepack_w13_layout
-    assert f(FAKE, FAKE, 2, 256, 256, 3, FAKE, FAKE, None) == 2       # unknown layout
-    assert f(FAKE, FAKE, 2, 256, 256, -1, FAKE, FAKE, None) == 2
+    assert f(FAKE, FAKE, 2, 256, 256, 3, FAKE, FAKE, None) == 4       # unknown layout
+    assert f(FAKE, FAKE, 2, 256, 256, -1, FAKE, FAKE, None) == 4
     assert f(FAKE, FAKE, 2, 256, 128, 2, FAKE, FAKE, None) == 2       # I % 256
     assert f(None, FAKE, 2, 256, 256, 2, FAKE, FAKE, None) == 1
     assert f(FAKE + 8, FAKE, 2, 256, 256, 1, FAKE, FAKE, None) == 3
@@ -143,16 +147,24 @@ def test_fc_validation(lib):
     bad = list(args); bad[16] = 16
     assert f1(*bad) == 5
     f2 = lib.moe_fc2_combine
-    args2 = [FAKE, FAKE, 4, 256, 128, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE,
-             1 << 30, None]
-    bad = list(args2); bad[13] = 128
+    # hq hs T H I top_k E_local offs sroute rrow w w2 w2_s mode out ld_out ws ws_bytes stream
+    args2 = [FAKE, FAKE, 4, 256, 128, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 256,
+             FAKE, 1 << 30, None]
+    bad = list(args2); bad[15] = 128
     assert f2(*bad) == 2                                                    # ld_out < H
-    bad = list(args2); bad[13] = 260
+    bad = list(args2); bad[15] = 260
     assert f2(*bad) == 3                                                    # ld_out % 8
-    bad = list(args2); bad[15] = 1024
+    bad = list(args2); bad[17] = 1024
     assert f2(*bad) == 5
     bad = list(args2); bad[12] = None
     assert f2(*bad) == 1
+    for mode in (2, -1, 99):                                                # unknown mode
+        bad = list(args2); bad[13] = mode
+        assert f2(*bad) == 4
+        tiled = list(bad); tiled[3] = 512; tiled[15] = 512                 # H % 512 for tiled
+        assert lib.moe_fc2_combine_tiled(*tiled) == 4
+    bad = list(args2); bad[13] = 1; bad[8] = None
+    assert f2(*bad) == 1                                                    # atomic needs routes
 
 
 def test_binding_rejects_cpu_tensors():
@@ -162,6 +174,71 @@ def test_binding_rejects_cpu_tensors():
         B.moe_route(torch.zeros(4, 8), None, 2)
     with pytest.raises(ValueError):
         B.moe_quant_mxfp8(torch.zeros(4, 128, dtype=torch.bfloat16))
+
+
+class _FakeCuda:
+    """Stands in for a device tensor in the binding's checks (they read only
+    dtype, is_cuda, device, shape and contiguity), so the shape checks that
+    guard the prepack launches can be exercised without a GPU."""
+
+    def __init__(self, shape, dtype):
+        import torch
+        self.t = torch.empty(shape, dtype=dtype)
+        self.shape, self.dtype, self.is_cuda, self.device = self.t.shape, dtype, True, "cuda:0"
+
+    def dim(self):
+        return self.t.dim()
+
+    def is_contiguous(self):
+        return True
+
+
+def test_binding_checks_prepack_scale_shapes(monkeypatch):
+    import torch
+    from mxfp8_mxfp4_experts_amd import _binding as B
+    monkeypatch.setattr(B, "_need", _need_fake(B._need))
+    w = _FakeCuda((2, 512, 128), torch.uint8)                 # E=2, N=512, K=256
+    for name in ("moe_prepack_w13", "moe_prepack_w2"):
+        fn = getattr(B, name)
+        for bad in ((2, 512, 4), (2, 256, 8), (1, 512, 8)):   # K/32 = 8 expected
+            with pytest.raises(ValueError):
+                fn(w, _FakeCuda(bad, torch.uint8))
+    with pytest.raises(ValueError):
+        B.moe_prepack_w13_layout(w, _FakeCuda((2, 512, 7), torch.uint8), B.W13_UP_GATE)
+    with pytest.raises(ValueError):                            # K/2 not a multiple of 16
+        B.moe_prepack_w2(_FakeCuda((2, 512, 100), torch.uint8), _FakeCuda((2, 512, 6), torch.uint8))
+
+
+def _need_fake(orig):
+    def need(t, name, dtype, shape=None, contiguous=True, device=None):
+        if isinstance(t, _FakeCuda):
+            if t.dtype != dtype:
+                raise ValueError(name)
+            if shape is not None and tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} must have shape {tuple(shape)}")
+            return
+        return orig(t, name, dtype, shape, contiguous, device)
+    return need
+
+
+def test_layer_checks_weight_shapes(monkeypatch):
+    import torch
+    from mxfp8_mxfp4_experts_amd import _binding as B
+    from mxfp8_mxfp4_experts_amd.layer import MoELayer
+    monkeypatch.setattr(B, "_need", _need_fake(B._need))
+    E, H, I = 2, 512, 256
+    good = dict(w13=((E, 2 * I, H // 2)), w13_s=((E, 2 * I, H // 32)), w2=((E, H, I // 2)),
+                w2_s=((E, H, I // 32)))
+    for key, shape in (("w13_s", (E, 2 * I, H // 64)), ("w2", (E, H, I)), ("w2", (E, I, H // 2)),
+                       ("w2_s", (E, H, I // 16))):
+        args = {k: _FakeCuda(v, torch.uint8) for k, v in good.items()}
+        args[key] = _FakeCuda(shape, torch.uint8)
+        with pytest.raises(ValueError):
+            MoELayer(args["w13"], args["w13_s"], args["w2"], args["w2_s"], top_k=2, E=E)
+    args = {k: _FakeCuda(v, torch.uint8) for k, v in good.items()}
+    with pytest.raises(ValueError):
+        MoELayer(args["w13"], args["w13_s"], args["w2"], args["w2_s"], top_k=2, E=E,
+                 combine="fused")
 
 
 def test_permute_noalloc_validation(lib):

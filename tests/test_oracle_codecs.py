@@ -155,3 +155,50 @@ def test_checkpoint_shapes_match_layout():
     assert f["w2.weight_packed"] == [H, I // 2] and f["w2.weight_scale"] == [H, I // 32]
     facts = json.load(open(GOLDEN))["x_sf_view"]
     assert facts["bytes_per_int32"] * facts["elements_per_scale"] == 128
+
+
+def test_f64_to_bf16_value_matches_torch_on_float32_inputs():
+    """The report-only bf16 rounding agrees with torch's own float32 ->
+    bfloat16 conversion (round to nearest, ties to even) on float32 values:
+    random magnitudes across the exponent range, exact bf16 midpoints (ties),
+    their float32 neighbours, subnormals, the largest finite values."""
+    import torch
+
+    from oracle.codecs import f64_to_bf16_value
+
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal(20000) * np.exp2(rng.integers(-130, 120, 20000))).astype(np.float32)
+    grid = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    grid = grid[np.isfinite(grid)]
+    mid = (grid.view(np.uint32) + np.uint32(0x8000)).view(np.float32)     # exact ties
+    mid = mid[np.isfinite(mid)]
+    near = np.concatenate([np.nextafter(mid, np.float32(np.inf)),
+                           np.nextafter(mid, np.float32(-np.inf))])
+    x = np.concatenate([v, mid, near, np.float32([3.3e38, -3.3e38, 1e-45, -1e-45, 0.0, -0.0])])
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    got = f64_to_bf16_value(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_f64_to_bf16_value_is_a_nearest_bf16_of_float64_inputs():
+    """On float64 values that are not float32 values, the result is a bf16
+    value no farther from the input than either bf16 neighbour of it, in
+    exact rational arithmetic (the float64 -> float32 -> bf16 double rounding
+    can only pick the other of two equally near values on an exact tie)."""
+    from fractions import Fraction
+
+    from oracle.codecs import f64_to_bf16_value
+
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal(3000) * np.exp2(rng.integers(-60, 60, 3000))
+    got = f64_to_bf16_value(v)
+    bits = got.astype(np.float32).view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)                       # a bf16 value
+    up = (bits + 0x10000).view(np.float32).astype(np.float64)
+    dn = (bits - 0x10000).view(np.float32).astype(np.float64)
+    for x, r, a, b in zip(v, got, up, dn):
+        d = abs(Fraction(float(r)) - Fraction(float(x)))
+        assert d <= abs(Fraction(float(a)) - Fraction(float(x)))
+        assert d <= abs(Fraction(float(b)) - Fraction(float(x)))

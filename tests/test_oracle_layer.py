@@ -289,3 +289,33 @@ def test_generator_weights_are_mxfp4_of_bf16_normals():
     r = np.abs(v).reshape(v.shape[0], -1, 32).max(-1) / sc
     assert np.all(r <= 6.0) and np.all(r >= 3.0)
     assert 0.01 < v.std() < 0.03
+
+
+def test_report_accumulators_agree_and_bound_the_sums():
+    """The report-only FC1 outputs: oracle_tokens' per-route accumulators and
+    |product| sums equal oracle_layer's rows, and every |accumulator| is at
+    most its sum of |products| (triangle inequality), with equality where
+    all products share a sign (a one-hot activation row)."""
+    cfg = synth.custom_config("s", 72, T=10, H=64, I=64, E=6, K=2, E_local=4, expert_offset=1)
+    case = synth.make_case(cfg)
+    w = _np_weights(case)
+    full = oracle.oracle_layer(case["x_bf16"], case["logits"], case["bias"], w["w13"], w["w13_s"],
+                               w["w2"], w["w2_s"], top_k=2, expert_offset=1, report=True)
+    assert np.all(np.abs(full["acc"]) <= full["absum"] * (1 + 1e-15))
+    sub = oracle.oracle_tokens([7, 2, 9], case["x_bf16"], full["topk_idx"], full["topk_w"],
+                               lambda e: (w["w13"][e], w["w13_s"][e], w["w2"][e], w["w2_s"][e]),
+                               top_k=2, expert_offset=1, E_local=4)
+    toks = [7, 2, 9]
+    for (j, k), (hq, hs, a, acc, absum) in sub["h"].items():
+        row = int(full["route_row"][toks[j] * 2 + k])
+        assert np.array_equal(hq, full["hq"][row]) and np.array_equal(hs, full["hs"][row])
+        np.testing.assert_allclose(acc, full["acc"][row], rtol=1e-13, atol=1e-300)
+        np.testing.assert_allclose(absum, full["absum"][row], rtol=1e-13, atol=1e-300)
+    # one-hot activation: x = 1.0 at column 5 only, so acc = deq(w[:, 5]) and
+    # absum = |acc| exactly
+    xb = np.zeros((1, 64), np.uint16)
+    xb[0, 5] = 0x3F80
+    one = oracle.oracle_layer(xb, None, None, w["w13"], w["w13_s"], w["w2"], w["w2_s"], top_k=1,
+                              topk_idx=np.array([[1]], np.int32),
+                              topk_w=np.array([[1.0]], np.float32), report=True)
+    assert np.array_equal(np.abs(one["acc"]), one["absum"])
