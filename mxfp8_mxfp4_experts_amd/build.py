@@ -2,8 +2,9 @@
 
 Run ``python -m mxfp8_mxfp4_experts_amd.build`` or call ``build()``.  Every
 source is compiled on each call (a cross-compile: no GPU is needed).
-``build_probes()`` also builds the test-only probe library
-(``tests/probe/libnumprobe.so``), which is never part of the layer.
+``build_rates()`` builds the benchmark's rate probes
+(``measure/libmi355rates.so``) and ``build_probes()`` the test-only probe
+library (``tests/probe/libnumprobe.so``); neither is part of the layer.
 """
 from __future__ import annotations
 
@@ -79,6 +80,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return _build_so(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), OUT, "lib", verbose, jobs)
 
 
+MEASURE_DIR = os.path.join(PKG, "measure")
+MEASURE_OUT = os.path.join(MEASURE_DIR, "libmi355rates.so")
+
+
+def build_rates(verbose: bool = False) -> str:
+    """The benchmark's achievable-rate probes (streaming HBM read, scaled
+    MFMA loop); not part of the layer library."""
+    return _build_so([os.path.join(MEASURE_DIR, "rates.hip")], MEASURE_OUT, "rates", verbose)
+
+
 PROBE_DIR = os.path.join(ROOT, "tests", "probe")
 PROBE_OUT = os.path.join(PROBE_DIR, "libnumprobe.so")
 
@@ -92,4 +103,5 @@ def build_probes(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     build(verbose=True)
+    build_rates(verbose=True)
     build_probes(verbose=True)

@@ -59,6 +59,17 @@ class MoELayer:
         self.device = w13.device
         self._alloc(max_tokens)
 
+    def with_combine(self, combine: str) -> "MoELayer":
+        """A layer sharing these (already prepacked) weights whose FC2 sums
+        with the other combine mode; it has buffers of its own."""
+        if combine not in ("deterministic", "atomic"):
+            raise ValueError('combine must be "deterministic" or "atomic"')
+        other = object.__new__(MoELayer)
+        other.__dict__.update(self.__dict__)
+        other.combine_mode = B.COMBINE_ATOMIC if combine == "atomic" else B.COMBINE_DETERMINISTIC
+        other._alloc(self.max_tokens)
+        return other
+
     def _alloc(self, T: int):
         dev, K, H, I = self.device, self.top_k, self.H, self.I
         R = T * K

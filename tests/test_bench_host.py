@@ -1,11 +1,15 @@
 """Host logic of bench.py (no GPU): the JSON contract's refusal of several
-GPUs and the key that ties committed traffic counters to the kernels' code."""
+GPUs, the key that ties committed traffic counters to the kernels' code, and
+the CPU baseline's sample."""
 import json
 import os
 import subprocess
 import sys
 
+import numpy as np
+
 import bench
+import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -27,3 +31,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_cpu_baseline_sample_reaches_sixteen_kept_routes():
+    cfg = synth.WORKLOADS["ep_share_T4096"]
+    rng = np.random.default_rng(0)
+    rid = rng.integers(0, 896, (cfg.T, cfg.K)).astype(np.int32)
+    n = bench._sample_tokens(cfg, rid, 16)
+    kept = (rid[:n] < cfg.E_local).sum()
+    assert kept >= 16 and (rid[:n - 1] < cfg.E_local).sum() < 16
+    full = synth.WORKLOADS["decode_T8"]
+    assert bench._sample_tokens(full, rng.integers(0, 896, (8, 16)).astype(np.int32), 16) == 1
+
+
+def test_host_record_names_the_cores():
+    hr = bench.host_record()
+    assert hr["host_cores"] == os.cpu_count()
