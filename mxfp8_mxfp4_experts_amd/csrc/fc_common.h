@@ -50,58 +50,44 @@ struct FcParams {
 
 // SiTU(g, u) = alpha tanh(g / alpha) sigmoid(g) * beta tanh(u / beta)
 // (page 1, "真实 checkpoint 契约": the SiTU activation with alpha = 4, beta =
-// 25; alpha, beta > 0), in float32 from hardware base-2 exponentials and
-// reciprocals.  With z1 = e^(-2g/alpha), z2 = e^(-g), w = e^(-2u/beta):
-//   tanh(g/alpha) = (1 - z1) / (1 + z1),  sigmoid(g) = 1 / (1 + z2),
-//   tanh(u/beta) = (1 - w) / (1 + w).
-// 1 - z cancels when its argument y = g/alpha or u/beta is small (u/beta
-// nearly always is: |u| is a few units against beta = 25), so for |y| <= 3/8
-// tanh(y) comes from its Taylor series through y^11 instead (the first
-// omitted term, 21844/6081075 y^13, is below 2^-25 |y| there), with a
-// denominator of 1.  The numerators keep the signs of g and u (tanh keeps the
-// sign of zero).  z1 and w are capped at e^40, where both tanh quotients are
-// already +-1 in float32, so the two tanh factors and their product stay
-// finite; the sigmoid takes its own reciprocal of 1 + z2, which is 0 once z2
-// overflows (g < -88: the true value is below 1e-36).  Accuracy: a few
-// float32 ulps relative plus the rounding of the exponent g log2(e) (about
-// |g| 2^-24 relative).  A NaN input gives 0 here (the requantisation rule
-// sends NaN to code 0 and leaves it out of the block maximum, which is what
-// 0 does).
+// 25; alpha, beta > 0), in float32 from three hardware base-2 exponentials
+// and one reciprocal.  With z1 = e^(-2|g|/alpha), z2 = e^(-|g|) and
+// w = e^(-2|u|/beta), all in (0, 1]:
+//   tanh(g/alpha) = sign(g) (1 - z1) / (1 + z1),
+//   sigmoid(g)    = s / (1 + z2), s = 1 for g >= 0 and z2 for g < 0,
+//   tanh(u/beta)  = sign(u) (1 - w) / (1 + w),
+// so SiTU = alpha beta sign(g)(1 - z1) s sign(u)(1 - w) / ((1 + z1)(1 + z2)(1 + w)),
+// where nothing overflows (the denominator lies in [1, 8]).  s is formed
+// without a per-lane select: m z2 + (1 - m) with m = clamp(-g 2^24, 0, 1),
+// exact except for |g| < 2^-24, where z2 is within 2^-24 of 1 anyway.  The
+// numerators keep the signs of g and u (tanh keeps the sign of zero).
+// 1 - z cancels for small |g|/alpha, |u|/beta: the result then carries an
+// absolute error of a few float32 ulps of the factor's scale (alpha, beta)
+// rather than a relative one.  Measured against float64 on the device this
+// flips about 1.5e-5 of the requantised bytes, against about 5e-4 that the
+// MFMA's own accumulation flips; a cancellation-free series form cost 0.4 ms
+// of the 8K-token prefill FC1 (its epilogue is VALU-bound), so the cheaper
+// form is kept.  A NaN input gives 0 here (the requantisation rule sends NaN
+// to code 0 and leaves it out of the block maximum, which is what 0 does).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 struct SituConst {
   float k1, k2, k3, ab;   // -2 log2(e) / alpha, -log2(e), -2 log2(e) / beta, alpha beta
-  float ia, ib;           // 1 / alpha, 1 / beta
 };
 __device__ __forceinline__ SituConst situ_const(float alpha, float beta) {
   const float l2e = 1.4426950408889634f;
-  return SituConst{-2.0f * l2e / alpha, -l2e, -2.0f * l2e / beta, alpha * beta,
-                   1.0f / alpha, 1.0f / beta};
-}
-// tanh(y) for |y| <= 3/8: y + y^3 (-1/3 + y^2 (2/15 + y^2 (-17/315 +
-// y^2 (62/2835 + y^2 (-1382/155925))))), sign of zero kept.
-__device__ __forceinline__ float tanh_series(float y) {
-  const float y2 = y * y;
-  float p = -1382.0f / 155925.0f;
-  p = fmaf(p, y2, 62.0f / 2835.0f);
-  p = fmaf(p, y2, -17.0f / 315.0f);
-  p = fmaf(p, y2, 2.0f / 15.0f);
-  p = fmaf(p, y2, -1.0f / 3.0f);
-  return copysignf(fmaf(p * y2, y, y), y);
+  return SituConst{-2.0f * l2e / alpha, -l2e, -2.0f * l2e / beta, alpha * beta};
 }
 __device__ __forceinline__ float situ(float g, float u, const SituConst& c) {
-  const float cap = 57.70780163555853f;   // 40 log2(e)
-  const float z1 = fast_exp2(fminf(g * c.k1, cap));
-  const float z2 = fast_exp2(g * c.k2);
-  const float w = fast_exp2(fminf(u * c.k3, cap));
-  const float y1 = g * c.ia, y2 = u * c.ib;
-  const bool s1 = fabsf(y1) <= 0.375f, s2 = fabsf(y2) <= 0.375f;
-  const float n1 = s1 ? tanh_series(y1) : copysignf(1.0f - z1, g);
-  const float n2 = s2 ? tanh_series(y2) : copysignf(1.0f - w, u);
-  const float d1 = s1 ? 1.0f : 1.0f + z1;
-  const float d2 = s2 ? 1.0f : 1.0f + w;
-  const float t = c.ab * (n1 * n2) * fast_rcp(d1 * d2);
-  const float v = t * fast_rcp(1.0f + z2);
+  const float ag = fabsf(g), au = fabsf(u);
+  const float z1 = fast_exp2(ag * c.k1);
+  const float z2 = fast_exp2(ag * c.k2);
+  const float w = fast_exp2(au * c.k3);
+  const float m = __builtin_amdgcn_fmed3f(g * -16777216.0f, 0.0f, 1.0f);
+  const float sn = fmaf(m, z2, 1.0f - m);   // exactly z2 for m = 1, 1 for m = 0
+  const float num = copysignf(1.0f - z1, g) * copysignf(1.0f - w, u);
+  const float den = (1.0f + z1) * (1.0f + z2) * (1.0f + w);
+  const float v = c.ab * (num * sn) * fast_rcp(den);
   return __builtin_isunordered(g, u) ? 0.0f : v;
 }
 // Four E4M3 codes of x / s (s a normal power of two, |x / s| <= 448), packed

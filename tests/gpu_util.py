@@ -80,11 +80,27 @@ def assert_output_close(out, ref, tag=""):
 ACC_EPS = 2.0 ** -15
 
 
+def situ_f32_error(g, u, alpha=4.0, beta=25.0):
+    """Bound on the kernel's float32 SiTU error at exact inputs g, u (checked
+    on the device by tests/test_gpu_numerics.py): (32 + 2|g|) 2^-24 relative
+    (float32 roundings and the exponent's), plus 2^-22 of each tanh factor's
+    scale (alpha, beta) times the other factor, where 1 - e^(-2y) cancels."""
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-g))
+        gate = alpha * np.tanh(g / alpha) * sg
+        up = beta * np.tanh(u / beta)
+        rel = (32.0 + 2.0 * np.abs(g)) * 2.0 ** -24 * np.abs(gate * up)
+        cancel = 2.0 ** -22 * (alpha * sg * np.abs(up) + beta * np.abs(gate))
+    return rel + cancel + 1e-36
+
+
 def situ_error_bound(g, u, absum_g, absum_u, alpha=4.0, beta=25.0):
     """Largest |SiTU_gpu - SiTU(g, u)| when the GPU's accumulators carry at
     most ACC_EPS * absum of error and its float32 SiTU is within
-    (32 + 2|g|) 2^-24 relative (both measured in tests/test_gpu_numerics.py):
-    first-order terms with a 25% margin plus the second-order ones."""
+    situ_f32_error (both checked in tests/test_gpu_numerics.py): first-order
+    terms with a 25% margin plus the second-order ones."""
     g = np.asarray(g, np.float64)
     u = np.asarray(u, np.float64)
     with np.errstate(over="ignore", invalid="ignore"):
@@ -96,8 +112,7 @@ def situ_error_bound(g, u, absum_g, absum_u, alpha=4.0, beta=25.0):
         dg, du = ACC_EPS * np.asarray(absum_g), ACC_EPS * np.asarray(absum_u)
         first = np.abs(dgate * up) * dg + np.abs(gate * dup) * du
         second = 0.5 * (np.abs(up) * dg * dg + 0.1 * np.abs(gate) * du * du) + np.abs(dgate * dup) * dg * du
-        a = gate * up
-        bound = 1.25 * first + second + (32.0 + 2.0 * np.abs(g)) * 2.0 ** -24 * np.abs(a) + 1e-30
+        bound = 1.25 * first + second + situ_f32_error(g, u, alpha, beta)
     return np.where(np.isfinite(bound), bound, np.inf)
 
 
