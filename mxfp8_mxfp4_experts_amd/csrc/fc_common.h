@@ -50,45 +50,56 @@ struct FcParams {
 
 // SiTU(g, u) = alpha tanh(g / alpha) sigmoid(g) * beta tanh(u / beta)
 // (page 1, "真实 checkpoint 契约": the SiTU activation with alpha = 4, beta =
-// 25; alpha, beta > 0), in float32 from three hardware base-2 exponentials
-// and one reciprocal.  With z1 = e^(-2|g|/alpha), z2 = e^(-|g|) and
-// w = e^(-2|u|/beta), all in (0, 1]:
+// 25; alpha, beta > 0), in float32 from hardware base-2 exponentials and
+// reciprocals.  With z1 = e^(-2|g|/alpha), z2 = e^(-|g|) and
+// w = e^(-2|u|/beta), all in [0, 1]:
 //   tanh(g/alpha) = sign(g) (1 - z1) / (1 + z1),
 //   sigmoid(g)    = s / (1 + z2), s = 1 for g >= 0 and z2 for g < 0,
 //   tanh(u/beta)  = sign(u) (1 - w) / (1 + w),
 // so SiTU = alpha beta sign(g)(1 - z1) s sign(u)(1 - w) / ((1 + z1)(1 + z2)(1 + w)),
-// where nothing overflows (the denominator lies in [1, 8]).  s is formed
-// without a per-lane select: m z2 + (1 - m) with m = clamp(-g 2^24, 0, 1),
-// exact except for |g| < 2^-24, where z2 is within 2^-24 of 1 anyway.  The
-// numerators keep the signs of g and u (tanh keeps the sign of zero).
-// 1 - z cancels for small |g|/alpha, |u|/beta: the result then carries an
-// absolute error of a few float32 ulps of the factor's scale (alpha, beta)
-// rather than a relative one.  Measured against float64 on the device this
-// flips about 1.5e-5 of the requantised bytes, against about 5e-4 that the
-// MFMA's own accumulation flips; a cancellation-free series form cost 0.4 ms
-// of the 8K-token prefill FC1 (its epilogue is VALU-bound), so the cheaper
-// form is kept.  A NaN input gives 0 here (the requantisation rule sends NaN
-// to code 0 and leaves it out of the block maximum, which is what 0 does).
+// where nothing overflows: each denominator lies in [1, 8], so two of them
+// share one reciprocal (SiTU values are computed in pairs).  With alpha = 4,
+// z2 = z1^2 saves an exponential.  s = max(z2, clamp(g 2^64, 0, 1)) needs no
+// per-lane select: 1 for g >= 2^-64, z2 for g <= 0, and z2 (within 2^-64 of
+// 1) in between.  The numerators keep the signs of g and u (tanh keeps the
+// sign of zero).  1 - z cancels for small |g|/alpha, |u|/beta: the result
+// then carries an absolute error of a few float32 ulps of the factor's scale
+// (alpha, beta) rather than a relative one.  Measured against float64 on the
+// device this flips about 1e-5 of the requantised bytes, against about 5e-4
+// that the MFMA's own accumulation flips; a cancellation-free series form
+// cost 0.4 ms of the 8K-token prefill FC1, whose epilogue is VALU-bound.  A
+// NaN input gives 0 here (the requantisation rule sends NaN to code 0 and
+// leaves it out of the block maximum, which is what 0 does).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 struct SituConst {
   float k1, k2, k3, ab;   // -2 log2(e) / alpha, -log2(e), -2 log2(e) / beta, alpha beta
+  bool a4;                // alpha == 4: e^(-|g|) = z1^2
 };
 __device__ __forceinline__ SituConst situ_const(float alpha, float beta) {
   const float l2e = 1.4426950408889634f;
-  return SituConst{-2.0f * l2e / alpha, -l2e, -2.0f * l2e / beta, alpha * beta};
+  return SituConst{-2.0f * l2e / alpha, -l2e, -2.0f * l2e / beta, alpha * beta, alpha == 4.0f};
 }
-__device__ __forceinline__ float situ(float g, float u, const SituConst& c) {
-  const float ag = fabsf(g), au = fabsf(u);
-  const float z1 = fast_exp2(ag * c.k1);
-  const float z2 = fast_exp2(ag * c.k2);
-  const float w = fast_exp2(au * c.k3);
-  const float m = __builtin_amdgcn_fmed3f(g * -16777216.0f, 0.0f, 1.0f);
-  const float sn = fmaf(m, z2, 1.0f - m);   // exactly z2 for m = 1, 1 for m = 0
-  const float num = copysignf(1.0f - z1, g) * copysignf(1.0f - w, u);
-  const float den = (1.0f + z1) * (1.0f + z2) * (1.0f + w);
-  const float v = c.ab * (num * sn) * fast_rcp(den);
-  return __builtin_isunordered(g, u) ? 0.0f : v;
+// One value's numerator and denominator (see above).
+template <bool A4>
+__device__ __forceinline__ void situ_parts(float g, float u, const SituConst& c, float& num,
+                                           float& den) {
+  const float z1 = fast_exp2(fabsf(g) * c.k1);
+  const float z2 = A4 ? z1 * z1 : fast_exp2(fabsf(g) * c.k2);
+  const float w = fast_exp2(fabsf(u) * c.k3);
+  const float s = fmaxf(z2, __builtin_amdgcn_fmed3f(g * 18446744073709551616.0f, 0.0f, 1.0f));
+  num = copysignf(1.0f - z1, g) * copysignf(1.0f - w, u) * s;
+  den = (1.0f + z1) * (1.0f + z2) * (1.0f + w);
+}
+template <bool A4>
+__device__ __forceinline__ void situ2(float g0, float u0, float g1, float u1, const SituConst& c,
+                                      float& v0, float& v1) {
+  float n0, d0, n1, d1;
+  situ_parts<A4>(g0, u0, c, n0, d0);
+  situ_parts<A4>(g1, u1, c, n1, d1);
+  const float r = c.ab * fast_rcp(d0 * d1);
+  v0 = __builtin_isunordered(g0, u0) ? 0.0f : n0 * d1 * r;
+  v1 = __builtin_isunordered(g1, u1) ? 0.0f : n1 * d0 * r;
 }
 // Four E4M3 codes of x / s (s a normal power of two, |x / s| <= 448), packed
 // little-endian, by the hardware scaled conversion.
@@ -132,11 +143,15 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
   if (FC1) {
     const int c0 = u * 32;
     const SituConst sc = situ_const(p.alpha, p.beta);
-    float a[8];
+    float a[8];   // a[r]: column c0 + 4g + r; a[4 + r]: column c0 + 16 + 4g + r
+    if (sc.a4) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      a[r] = situ(acc[0][r], acc[2][r], sc);       // column c0 + 4g + r
-      a[4 + r] = situ(acc[1][r], acc[3][r], sc);   // column c0 + 16 + 4g + r
+      for (int r = 0; r < 4; ++r)
+        situ2<true>(acc[0][r], acc[2][r], acc[1][r], acc[3][r], sc, a[r], a[4 + r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        situ2<false>(acc[0][r], acc[2][r], acc[1][r], acc[3][r], sc, a[r], a[4 + r]);
     }
     float amax = 0.0f;
 #pragma unroll

@@ -5,7 +5,7 @@
 //   * probe_mfma_w4a8: the block-scaled 16x16x128 MFMA wrapper (E2M1 weights
 //     x E4M3 tokens, E8M0 scales per 32 K) accumulated over K as the FC
 //     kernels do, raw float32 accumulators out;
-//   * probe_situ: the FC1 epilogue's float32 SiTU;
+//   * probe_situ: the FC1 epilogue's float32 SiTU (in pairs, as there);
 //   * probe_e4m3_scaled: the FC1 epilogue's hardware scaled E4M3 conversion
 //     next to the library's integer encoder.
 // Every launch covers exactly the elements the host sizes describe.
@@ -43,13 +43,22 @@ __global__ __launch_bounds__(64) void mfma_probe_kernel(const uint8_t* __restric
   for (int r = 0; r < 4; ++r) out[((size_t)blockIdx.x * 16 + 4 * g + r) * 16 + li] = acc[r];
 }
 
+// Thread i computes elements 2i and 2i + 1 as one pair (the epilogue's
+// shared reciprocal), with the alpha = 4 shortcut where it applies.
 __global__ __launch_bounds__(256) void situ_probe_kernel(const float* __restrict__ gv,
-                                                         const float* __restrict__ uv, int n,
+                                                         const float* __restrict__ uv, int n2,
                                                          float alpha, float beta,
                                                          float* __restrict__ out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  out[i] = situ(gv[i], uv[i], situ_const(alpha, beta));
+  if (i >= n2) return;
+  const SituConst c = situ_const(alpha, beta);
+  float v0, v1;
+  if (c.a4)
+    situ2<true>(gv[2 * i], uv[2 * i], gv[2 * i + 1], uv[2 * i + 1], c, v0, v1);
+  else
+    situ2<false>(gv[2 * i], uv[2 * i], gv[2 * i + 1], uv[2 * i + 1], c, v0, v1);
+  out[2 * i] = v0;
+  out[2 * i + 1] = v1;
 }
 
 // Thread i converts x[4i .. 4i+3] at scale 2^e[i] (a normal power of two).
@@ -84,10 +93,12 @@ int probe_mfma_w4a8(const uint8_t* w, const uint8_t* ws, const uint8_t* a, const
   return check(hipGetLastError());
 }
 
+// n even.
 int probe_situ(const float* g, const float* u, int n, float alpha, float beta, float* out,
                hipStream_t stream) {
-  if (n <= 0) return 2;
-  hipLaunchKernelGGL(situ_probe_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, g, u, n,
+  if (n <= 0 || n % 2 != 0) return 2;
+  const int n2 = n / 2;
+  hipLaunchKernelGGL(situ_probe_kernel, dim3((n2 + 255) / 256), dim3(256), 0, stream, g, u, n2,
                      alpha, beta, out);
   return check(hipGetLastError());
 }

@@ -115,20 +115,21 @@ def situ_float32_bound(g, u, alpha=4.0, beta=25.0):
     return situ_f32_error(g, u, alpha, beta)
 
 
-def test_situ_float32_against_float64(probe):
+@pytest.mark.parametrize("alpha,beta", [(4.0, 25.0), (2.0, 10.0)])
+def test_situ_float32_against_float64(probe, alpha, beta):
     g, u = _situ_inputs()
     n = g.size
     gd, ud = torch.from_numpy(g).to(DEV), torch.from_numpy(u).to(DEV)
     out = torch.empty(n, dtype=torch.float32, device=DEV)
-    assert probe.probe_situ(gd.data_ptr(), ud.data_ptr(), n, 4.0, 25.0, out.data_ptr(),
+    assert probe.probe_situ(gd.data_ptr(), ud.data_ptr(), n, alpha, beta, out.data_ptr(),
                             _stream()) == 0
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    ref = oracle.situ(g.astype(np.float64), u.astype(np.float64))
+    ref = oracle.situ(g.astype(np.float64), u.astype(np.float64), alpha, beta)
     err = np.abs(got - ref)
     rel = err / np.maximum(np.abs(ref), 1e-30)
     n_rand = 1 << 20
-    print(f"[situ] float32 vs float64: max rel {rel.max():.3g}, median rel "
+    print(f"[situ alpha={alpha}] float32 vs float64: max rel {rel.max():.3g}, median rel "
           f"{np.median(rel[:n_rand]):.3g}, p99.9 {np.quantile(rel[:n_rand], 0.999):.3g}",
           flush=True)
     # requantised bytes this error alone flips (rows of 3584 = 112 groups of 32)
@@ -140,7 +141,7 @@ def test_situ_float32_against_float64(probe):
     flips = float(np.mean(q_ref != q_got))
     print(f"[situ] requantised bytes flipped by the float32 SiTU alone: {flips:.3g}", flush=True)
     assert np.all(np.isfinite(got))
-    bound = situ_float32_bound(g.astype(np.float64), u.astype(np.float64))
+    bound = situ_float32_bound(g.astype(np.float64), u.astype(np.float64), alpha, beta)
     worst = int(np.argmax(err / bound))
     print(f"[situ] worst error / bound: {err[worst] / bound[worst]:.3g}", flush=True)
     assert np.all(err <= bound), (g[worst], u[worst], got[worst], ref[worst])
