@@ -13,12 +13,13 @@ with HIP events on its launch stream), the deterministic and the atomic
 combine, and the CPU oracle timed on a bounded sample.  ``--workload NAME``
 runs one workload (the profiling runs use it).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rounds R]
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import glob
 import hashlib
 import re
@@ -401,17 +402,41 @@ def workload_record(run, ms_per_step, fc1_ms, wall, atomic_ms):
     return rec
 
 
-def bench_workload(name, w_all, dev, args, with_cpu, cpu_runs):
+def setup_runs(names, w_all, dev):
+    """One Run per workload.  The 896-expert workloads (T = 8, 256, 8192)
+    share one layer (one prepacked copy of the weights, buffers for the
+    largest T); the others get their own."""
     import torch
 
-    cfg = WORKLOADS[name]
-    t0 = time.perf_counter()
-    layer, w = make_layer(cfg, w_all, dev)
-    run = Run(name, cfg, layer, w, dev)
-    print(f"[bench] {name}: setup {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
-    ms, fc1_ms, wall = run.time_steps(layer, args.steps, args.warmup)
+    runs, shared = {}, None
+    for name in names:
+        cfg = WORKLOADS[name]
+        t0 = time.perf_counter()
+        full = cfg.H == 7168 and cfg.E_local == 896 and cfg.expert_offset == 0
+        if full and shared is None:
+            big = max(WORKLOADS[n].T for n in names
+                      if WORKLOADS[n].H == 7168 and WORKLOADS[n].E_local == 896)
+            shared = make_layer(dataclasses.replace(cfg, T=big), w_all, dev)
+        layer, w = shared if full else make_layer(cfg, w_all, dev)
+        runs[name] = Run(name, cfg, layer, w, dev)
+        print(f"[bench] {name}: setup {time.perf_counter() - t0:.1f}s", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    return runs
+
+
+def finish_run(run, round_times, args, with_cpu, cpu_runs):
+    """The timed rounds' record, the check against MoELayer, the atomic
+    combine's step time and the CPU baseline."""
+    import torch
+
+    cfg, layer, name = run.cfg, run.layer, run.name
+    ms = float(np.median([r[0] for r in round_times]))
+    fc1_ms = float(np.mean([r[1] for r in round_times]))
+    wall = float(sum(r[2] for r in round_times))
+    # The timed calls must compute what the layer computes (the last timed
+    # step left this workload's output in run.out).
+    run.step(layer)
     det = run.out.clone()
-    # The timed calls must compute what the layer computes.
     ref = layer(run.x, run.logits, run.bias,
                 topk_idx=layer.topk_idx[:cfg.T].clone() if run.given else None,
                 topk_w=layer.topk_w[:cfg.T].clone() if run.given else None)
@@ -428,15 +453,18 @@ def bench_workload(name, w_all, dev, args, with_cpu, cpu_runs):
         if not d <= 4e-2 * rms:
             raise SystemExit(f"[bench] {name}: atomic combine off by {d} (RMS {rms})")
         del alayer
+        torch.cuda.empty_cache()
     rec = workload_record(run, ms, fc1_ms, wall, atomic_ms)
+    if len(round_times) > 1:
+        r_ms = [r[0] for r in round_times]
+        rec["rounds"] = {"n": len(r_ms), "ms_per_step": [round(v, 5) for v in r_ms],
+                         "max_over_min": round(max(r_ms) / min(r_ms), 4)}
     if with_cpu:
         rid = layer.topk_idx[:cfg.T].cpu().numpy()
         rw = layer.topk_w[:cfg.T].cpu().numpy()
-        rec["cpu_baseline"] = cpu_baseline(cfg, run.act, w, rid, rw, cpu_runs(name))
+        rec["cpu_baseline"] = cpu_baseline(cfg, run.act, run.w, rid, rw, cpu_runs(name))
     print(f"[bench] {name}: {rec['ms_per_step']} ms/step, FC1 {rec['roofline']['frac']} of "
           f"{rec['roofline']['bound']}", file=sys.stderr, flush=True)
-    del run, layer
-    torch.cuda.empty_cache()
     return rec
 
 
@@ -447,6 +475,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
                     help="run this workload alone (default: the five-workload suite)")
+    ap.add_argument("--rounds", type=int, default=1,
+                    help="timed rounds of --steps steps, each round timing every workload in "
+                         "turn; a workload's step time is the median of its rounds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-combine timing")
     ap.add_argument("--no-rates", action="store_true", help="skip the achievable-rate probes")
@@ -476,7 +507,12 @@ def main():
         # median of 3 for the small and decode workloads, one run above
         return 3 if WORKLOADS[name].T <= 256 else 1
 
-    recs = {n: bench_workload(n, w_all, dev, args, not args.no_cpu_baseline, cpu_runs)
+    runs = setup_runs(names, w_all, dev)
+    times = {n: [] for n in names}
+    for _ in range(args.rounds):          # rounds interleave the workloads
+        for n in names:
+            times[n].append(runs[n].time_steps(runs[n].layer, args.steps, args.warmup))
+    recs = {n: finish_run(runs[n], times[n], args, not args.no_cpu_baseline, cpu_runs)
             for n in names}
     head = recs[names[0]]
     cfg = WORKLOADS[names[0]]
@@ -504,7 +540,7 @@ def main():
     if "cpu_baseline" in head:
         res["cpu_baseline"] = head["cpu_baseline"]
     res["layer"] = head["layer"]
-    for k in ("combine_atomic", "pages_ratio"):
+    for k in ("combine_atomic", "pages_ratio", "rounds"):
         if k in head:
             res[k] = head[k]
     if len(names) > 1:
