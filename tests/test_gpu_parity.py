@@ -213,14 +213,15 @@ def _check_tile_schedule(ws, counts, E_local):
     exclusive prefix of ceil(count / height) over the experts, then the expert
     of every 32-row tile."""
     words = to_np(ws.view(torch.int32))
-    for i, height in enumerate((32, 256)):
+    heights = (32, 256)
+    for i, height in enumerate(heights):
         tiles = (counts + height - 1) // height
         ref = np.concatenate([[0], np.cumsum(tiles)])
         got = words[i * (E_local + 1):(i + 1) * (E_local + 1)]
         assert np.array_equal(got, ref), f"tile prefix {height}"
     tiles32 = (counts + 31) // 32
     ref_map = np.repeat(np.arange(E_local, dtype=np.int32), tiles32)
-    start = 2 * (E_local + 1)
+    start = len(heights) * (E_local + 1)
     assert np.array_equal(words[start:start + len(ref_map)], ref_map), "tile -> expert map"
 
 
@@ -409,9 +410,11 @@ def test_one_hot_expert_spanning_many_tiles():
 @pytest.mark.parametrize("tiled", [True, False])
 def test_prefill_row_counts_at_layout_bounds(tiled):
     # Experts whose row counts sit on both sides of the prefill kernel's
-    # 16-row tile, 64 / 128-row stage layouts and 256-row item bounds, their
-    # rows scattered over the tokens (K = 1).
-    counts = [1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 320]
+    # 16-row tile, 64 / 128-row stage layouts and 256-row item bounds (and
+    # experts of two and three items), their rows scattered over the tokens
+    # (K = 1).
+    counts = [1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320,
+              384, 385, 401]
     T = sum(counts)
     cfg = synth.custom_config("bounds", 307, T=T, H=512, I=256, E=len(counts), K=1)
     act, w_np, w_dev = _small_case(cfg)
