@@ -6,8 +6,8 @@
 //     x E4M3 tokens, E8M0 scales per 32 K) accumulated over K as the FC
 //     kernels do, raw float32 accumulators out;
 //   * probe_situ: the FC1 epilogue's float32 SiTU (in pairs, as there);
-//   * probe_e4m3_scaled: the FC1 epilogue's hardware scaled E4M3 conversion
-//     next to the library's integer encoder.
+//   * probe_e4m3_scaled: the hardware scaled E4M3 conversion (FC1 epilogue,
+//     activation quantisation) next to the library's integer encoder.
 // Every launch covers exactly the elements the host sizes describe.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
