@@ -38,6 +38,7 @@ __host__ __device__ inline int64_t tile_map_entries(int64_t R, int E_local) {
 // spread the ranking; the per-expert scan over chunks reads them in batches).
 constexpr int kPermSingle = 2048;
 constexpr int kSchedStride = 64;   // int32 stride between the per-XCD work counters
+constexpr int kSchedItemPrefix = 9 * kSchedStride;   // int32 offset of the item prefix
 __host__ __device__ inline int perm_chunk_size(int64_t R) { return R <= 16384 ? 256 : 512; }
 inline int perm_chunks(int64_t R) {
   return R <= kPermSingle ? 0 : (int)((R + perm_chunk_size(R) - 1) / perm_chunk_size(R));
@@ -48,7 +49,8 @@ struct WsLayout {
                         // int32 [tile_map_entries(T * top_k, E_local)]
   size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
   size_t fc_sched;      // int32 [9][kSchedStride]: per-XCD work counters of the prefill FC
-                        // kernels, then their 9 item-range bounds
+                        // kernels, then their 9 item-range bounds; then int32 [E_local + 1]:
+                        // the prefix of the experts' work items
   size_t act_st;        // uint32 [max(H, I) / 128][T * top_k]: an FC input's scale dwords,
                         // stage-major in grouped-row order (prefill-shaped FC kernels)
   size_t y;             // deterministic combine: fp16 [T * top_k][H] (FC2 rows before the
@@ -69,7 +71,7 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I, bool atom
   l.perm_counts = off;
   off = align256(off + sizeof(int32_t) * (size_t)perm_chunks((int64_t)T * top_k) * E_local);
   l.fc_sched = off;
-  off = align256(off + sizeof(int32_t) * 9 * kSchedStride);
+  off = align256(off + sizeof(int32_t) * (kSchedItemPrefix + E_local + 1));
   l.act_st = off;
   off = align256(off + (size_t)T * top_k * (size_t)((H > I ? H : I) / 32));
   l.y = off;

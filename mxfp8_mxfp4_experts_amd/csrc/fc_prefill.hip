@@ -158,46 +158,77 @@ struct AOp {
 // writes its per-XCD item ranges.
 // Items of one FC launch, split over the 8 XCDs by estimated work: an item
 // (expert e, column group, 256-row tile) costs about kItemFixedRows + its rows
-// rounded up to 16 per stage.  Workgroup 0 of the pre-pass scans the
-// per-expert work (n_cg column groups of its tiles) and writes the first item
-// of each XCD's range (at a column-group boundary) to bounds[0..8].
+// rounded up to 16 per stage.  An expert with at most 64 rows has n_cg / 2
+// items (each two column groups), one with more n_cg items per 256-row tile.
+// Workgroup 0 of the pre-pass scans the per-expert work and item counts,
+// writes the item prefix over the experts to item_prefix[0..E_local] and the
+// first item of each XCD's range (at a column-group boundary) to
+// bounds[0..8].
 constexpr int kItemFixedRows = 64;
 constexpr int kTileGroup = 4;   // tiles per item group of a multi-tile expert
 
+__device__ __forceinline__ int expert_items(int rows, int n_tiles, int n_cg) {
+  return rows == 0 ? 0 : rows <= 64 ? n_cg / 2 : n_tiles * n_cg;
+}
+
 __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __restrict__ prefix,
-                            int E_local, int n_cg, int32_t* __restrict__ bounds) {
+                            int E_local, int n_cg, int32_t* __restrict__ bounds,
+                            int32_t* __restrict__ item_prefix) {
   __shared__ long long cum_s[kMaxLdsExperts + 1];
+  __shared__ int items_s[kMaxLdsExperts + 1];
   __shared__ long long wsum_s[4];
+  __shared__ int isum_s[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = (E_local + 255) / 256, e0 = tid * per;
   long long mine = 0;
+  int mine_items = 0;
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     const int c = offs[e + 1] - offs[e], nt = prefix[e + 1] - prefix[e];
     const long long w = (long long)n_cg * (nt * kItemFixedRows + 16 * ((c + 15) / 16));
-    cum_s[e + 1] = w;   // turned into a running sum below
+    cum_s[e + 1] = w;   // turned into running sums below
+    items_s[e + 1] = expert_items(c, nt, n_cg);
     mine += w;
+    mine_items += items_s[e + 1];
   }
-  // Exclusive scan of the 256 threads' sums: within each wavefront, then
+  // Exclusive scans of the 256 threads' sums: within each wavefront, then
   // plus the totals of the wavefronts before it.
   long long incl = mine;
+  int incl_items = mine_items;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const long long y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
+    const int yi = __shfl_up(incl_items, off);
+    if (lane >= off) {
+      incl += y;
+      incl_items += yi;
+    }
   }
-  if (lane == 63) wsum_s[wv] = incl;
-  if (tid == 0) cum_s[0] = 0;
+  if (lane == 63) {
+    wsum_s[wv] = incl;
+    isum_s[wv] = incl_items;
+  }
+  if (tid == 0) {
+    cum_s[0] = 0;
+    items_s[0] = 0;
+  }
   __syncthreads();
   long long run = incl - mine;
-  for (int w = 0; w < wv; ++w) run += wsum_s[w];
+  int run_items = incl_items - mine_items;
+  for (int w = 0; w < wv; ++w) {
+    run += wsum_s[w];
+    run_items += isum_s[w];
+  }
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     run += cum_s[e + 1];
     cum_s[e + 1] = run;
+    run_items += items_s[e + 1];
+    items_s[e + 1] = run_items;
   }
   __syncthreads();
+  for (int e = tid; e <= E_local; e += 256) item_prefix[e] = items_s[e];
   if (tid <= 8) {
     const long long total = cum_s[E_local];
-    const int n_items = prefix[E_local] * n_cg;
+    const int n_items = items_s[E_local];
     int item = tid == 8 ? n_items : 0;
     if (tid > 0 && tid < 8 && total > 0) {
       const long long target = total * tid / 8;
@@ -206,11 +237,11 @@ __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __r
         const int mid = (lo + hi) >> 1;
         if (cum_s[mid] <= target) lo = mid; else hi = mid;
       }
-      const int e = lo, nt = prefix[e + 1] - prefix[e];
+      const int e = lo, nt = prefix[e + 1] - prefix[e], c = offs[e + 1] - offs[e];
       const long long per_cg = nt > 0 ? (cum_s[e + 1] - cum_s[e]) / n_cg : 1;
       long long cg = per_cg > 0 ? (target - cum_s[e]) / per_cg : 0;
       cg = cg < n_cg ? cg : n_cg;
-      item = prefix[e] * n_cg + (int)cg * nt;
+      item = items_s[e] + (c <= 64 ? (int)cg / 2 : (int)cg * nt);
     }
     bounds[tid] = item;
   }
@@ -227,7 +258,7 @@ __global__ __launch_bounds__(256) void stage_scales_kernel(const uint8_t* __rest
   // ranges.
   if (blockIdx.x == 0) {
     if (threadIdx.x < 8) sched[threadIdx.x * kSchedStride] = 0;
-    split_items(offs, prefix, E_local, n_cg, sched + 8 * kSchedStride);
+    split_items(offs, prefix, E_local, n_cg, sched + 8 * kSchedStride, sched + kSchedItemPrefix);
   }
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= offs[E_local]) return;
@@ -501,7 +532,7 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
   const int K = p.K;
   const int n_stages = K / kKS;
   for (int i = tid; i <= p.E_local; i += kThreads) {
-    prefix_s[i] = p.tile_prefix[i];
+    prefix_s[i] = p.sched[kSchedItemPrefix + i];
     offs_s[i] = p.expert_offsets[i];
   }
   __syncthreads();
@@ -532,20 +563,14 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(item_s[0]);
     if (item >= item_hi || item < item_lo) break;
-    const int e = __builtin_amdgcn_readfirstlane(find_expert_lds(prefix_s, p.E_local, item / n_cg));
-    const int pe = __builtin_amdgcn_readfirstlane(prefix_s[e]);
-    const int nt = __builtin_amdgcn_readfirstlane(prefix_s[e + 1]) - pe;
-    const int local = item - pe * n_cg;
+    const int e = __builtin_amdgcn_readfirstlane(find_expert_lds(prefix_s, p.E_local, item));
+    const int local = item - __builtin_amdgcn_readfirstlane(prefix_s[e]);
     // An expert with at most 64 rows (one tile) runs as pairs of column
-    // groups: item i < n_cg / 2 of its range takes column groups 2 i and
-    // 2 i + 1, and the rest of its range is empty.
+    // groups: its item i takes column groups 2 i and 2 i + 1.
     const int e_rows = __builtin_amdgcn_readfirstlane(offs_s[e + 1]) -
                        __builtin_amdgcn_readfirstlane(offs_s[e]);
     const bool pair = e_rows <= 64;
-    if (pair && local >= (n_cg >> 1)) {
-      __syncthreads();   // every wavefront has read item_s before it is rewritten
-      continue;
-    }
+    const int nt = (e_rows + kBM - 1) / kBM;
     // Items of an expert run in groups of kTileGroup tiles: within a group,
     // column group by column group, tile by tile.  The items in flight then
     // cover about 8 column groups x 4 tiles of a hot expert (its weights
