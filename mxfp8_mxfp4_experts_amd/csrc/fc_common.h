@@ -201,14 +201,23 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
     // lanes with this li) share one power-of-two scale 2^e chosen so that the
     // largest finite magnitude lands in [2^14, 2^15): fp16 keeps every value
     // to 2^-11 relative (non-finite values stay non-finite).
+    // The largest finite magnitude: a plain maximum (NaN ignored), and the
+    // finite-only scan again in the rare lane whose maximum is infinite.
     float amax = 0.0f;
 #pragma unroll
     for (int bk = 0; bk < 4; ++bk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = fabsf(acc[bk][r]);
-        amax = (v <= 3.4028235e38f && v > amax) ? v : amax;   // finite values only
-      }
+      for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(acc[bk][r]));
+    if (amax > 3.4028235e38f) {
+      amax = 0.0f;
+#pragma unroll
+      for (int bk = 0; bk < 4; ++bk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = fabsf(acc[bk][r]);
+          amax = (v <= 3.4028235e38f && v > amax) ? v : amax;
+        }
+    }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     const int fe = (int)((__float_as_uint(amax) >> 23) & 0xFF);
