@@ -8,6 +8,8 @@ namespace mi355moe {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // One 16x16x128 block-scaled MFMA: A = 16 weight rows of E2M1 (cbsz 4), B = 16
 // token columns of E4M3 (blgp 0), with this lane's E8M0 scale bytes selected by J.
@@ -111,6 +113,20 @@ __device__ __forceinline__ uint32_t e4m3x4_scaled(float x0, float x1, float x2, 
   return __builtin_bit_cast(uint32_t, both);
 }
 
+// max(v, v of lane l ^ 16) and then with lane l ^ 32, by gfx950's cross-row
+// lane swaps (no trip through the LDS crossbar): swapping a register's odd
+// 16-lane rows with a copy's even rows leaves each lane holding its own value
+// in one result and its xor-16 partner's in the other (the same for halves
+// and xor 32).  Every lane must call this.
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const float m = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t c = __float_as_uint(m);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // The MFMAs read operands from all 64 lanes: make the accumulators live here,
 // with every lane active, so no MFMA is moved into per-lane store conditions.
 __device__ __forceinline__ void pin_acc(v4f (&acc)[4]) {
@@ -159,8 +175,7 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
       const float v = fabsf(a[i]);
       amax = v > amax ? v : amax;
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = max_over_lane_groups(amax);
     const int ex = mx8_exponent(amax);
     uint32_t q0 = 0, q1 = 0;
     if (ex > -127) {
@@ -218,19 +233,19 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
           amax = (v <= 3.4028235e38f && v > amax) ? v : amax;
         }
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = max_over_lane_groups(amax);
     const int fe = (int)((__float_as_uint(amax) >> 23) & 0xFF);
     const int e = fe - 141 < -128 ? -128 : fe - 141;
     if (valid) {
       uint16_t* dst = p.y + (size_t)row * p.N + u * 64 + 4 * g;
 #pragma unroll
       for (int bk = 0; bk < 4; ++bk) {
-        uint32_t h[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          h[r] = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(acc[bk][r], -e));
-        *reinterpret_cast<uint2*>(dst + 16 * bk) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        // Two values per conversion (round to nearest even, as one at a time).
+        const f32x2 lo = {ldexpf(acc[bk][0], -e), ldexpf(acc[bk][1], -e)};
+        const f32x2 hi = {ldexpf(acc[bk][2], -e), ldexpf(acc[bk][3], -e)};
+        *reinterpret_cast<uint2*>(dst + 16 * bk) =
+            uint2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2)),
+                  __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, f16x2))};
       }
       if (g == 0) p.ye[(size_t)row * (p.N / 64) + u] = (int8_t)e;
     }
