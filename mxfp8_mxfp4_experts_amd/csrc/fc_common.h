@@ -169,12 +169,9 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
       for (int r = 0; r < 4; ++r)
         situ2<false>(acc[0][r], acc[2][r], acc[1][r], acc[3][r], sc, a[r], a[4 + r]);
     }
-    float amax = 0.0f;
+    float amax = 0.0f;   // a NaN value (none: SiTU gives 0 for NaN input) would be skipped
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = fabsf(a[i]);
-      amax = v > amax ? v : amax;
-    }
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
     amax = max_over_lane_groups(amax);
     const int ex = mx8_exponent(amax);
     uint32_t q0 = 0, q1 = 0;
