@@ -233,17 +233,43 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
     amax = max_over_lane_groups(amax);
     const int fe = (int)((__float_as_uint(amax) >> 23) & 0xFF);
     const int e = fe - 141 < -128 ? -128 : fe - 141;
-    if (valid) {
-      uint16_t* dst = p.y + (size_t)row * p.N + u * 64 + 4 * g;
+    // fp16 pairs d[bk][h]: columns 16 bk + 4 g + 2 h, +1 of the row.
+    uint32_t d[4][2];
 #pragma unroll
-      for (int bk = 0; bk < 4; ++bk) {
-        // Two values per conversion (round to nearest even, as one at a time).
-        const f32x2 lo = {ldexpf(acc[bk][0], -e), ldexpf(acc[bk][1], -e)};
-        const f32x2 hi = {ldexpf(acc[bk][2], -e), ldexpf(acc[bk][3], -e)};
-        *reinterpret_cast<uint2*>(dst + 16 * bk) =
-            uint2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2)),
-                  __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, f16x2))};
+    for (int bk = 0; bk < 4; ++bk) {
+      // Two values per conversion (round to nearest even, as one at a time).
+      const f32x2 lo = {ldexpf(acc[bk][0], -e), ldexpf(acc[bk][1], -e)};
+      const f32x2 hi = {ldexpf(acc[bk][2], -e), ldexpf(acc[bk][3], -e)};
+      d[bk][0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, f16x2));
+      d[bk][1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, f16x2));
+    }
+    // Rotate the pieces among the four lanes of the row so that lane g ends
+    // up with columns 8 g .. 8 g + 7 and 32 + 8 g .. 32 + 8 g + 7: piece
+    // (lane group a1 a0, block k1 k0) moves to lane group k0 a1, block
+    // k1 a0.  Two exchanges do it: lane-group bit 1 with block bit 0 (32-lane
+    // swap), then lane-group bit 0 with block bit 0 (16-lane swap).
+#pragma unroll
+    for (int k1 = 0; k1 < 2; ++k1)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto r = __builtin_amdgcn_permlane32_swap(d[2 * k1][h], d[2 * k1 + 1][h], false, false);
+        d[2 * k1][h] = r[0];
+        d[2 * k1 + 1][h] = r[1];
       }
+#pragma unroll
+    for (int k1 = 0; k1 < 2; ++k1)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto r = __builtin_amdgcn_permlane16_swap(d[2 * k1][h], d[2 * k1 + 1][h], false, false);
+        d[2 * k1][h] = r[0];
+        d[2 * k1 + 1][h] = r[1];
+      }
+    if (valid) {
+      uint16_t* dst = p.y + (size_t)row * p.N + u * 64 + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        *reinterpret_cast<uint4*>(dst + 32 * s) =
+            uint4{d[2 * s][0], d[2 * s][1], d[2 * s + 1][0], d[2 * s + 1][1]};
       if (g == 0) p.ye[(size_t)row * (p.N / 64) + u] = (int8_t)e;
     }
   }

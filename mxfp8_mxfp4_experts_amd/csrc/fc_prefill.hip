@@ -24,10 +24,11 @@
 //     past the last stage the final stage is reloaded to keep that count.
 //     The loads sit in MFMA slots early in the stage (the longest lead before
 //     their wait);
-//   * an expert with at most 64 rows takes two column groups per item, so the
-//     token rows loaded for a stage feed both weight tiles (the per-CU load
-//     path, not HBM, bounds these items; token rows were a third of their
-//     bytes);
+//   * an expert with at most 128 rows takes two column groups per item, so
+//     the token rows loaded for a stage feed both weight tiles (the per-CU
+//     load path, not HBM, bounds these items; token rows were a third to a
+//     half of their bytes), and an item of 128 rows x 512 weight rows has a
+//     full tile's accumulators and bytes per MFMA;
 //   * the token scale dwords are first restaged (stage_scales_kernel) into a
 //     stage-major array in grouped-row order, so a tile's scales for one stage
 //     are one contiguous 1 KB run instead of one cache line per row: the
@@ -82,20 +83,22 @@ static_assert(tile_rows(kTilePrefixIndex) == kBM && kTilePrefixIndex < kNumTileS
 // token or the weight scale dwords); when stage s + 1 is waited for, the
 // loads of the kAhead - 1 stages after it stay in flight.
 //
-// PAIR (P = 1 only): the item covers two column groups of an expert with at
-// most 64 rows, so one stage's token rows feed both weight tiles and the
-// token bytes per weight byte halve: [token rows 8 KB][token scale dwords
-// 2 KB][weights of both column groups 32 KB][their scale dwords 2 KB], 3
+// PAIR (P = 1 or 2): the item covers two column groups of an expert with at
+// most 64 P rows, so one stage's token rows feed both weight tiles and the
+// token bytes per weight byte halve: [token rows 8P KB][token scale dwords
+// P/4 KB][weights of both column groups 32 KB][their scale dwords 2 KB], 3
 // stages loaded 2 ahead.  Wavefront w works on column group w >> 2 of the
 // pair, weight half w & 1 and the token tiles (w >> 1) & 1 + 2 j; it issues
-// 7 loads per stage (a token piece, 4 weight pieces, a weight and a token
-// scale piece).
+// P + 6 loads per stage (P token pieces, 4 weight pieces, a weight and a
+// token scale piece; the token scale pieces of wavefronts w and w + P are
+// the same bytes).
 template <int P, bool PAIR = false>
 struct Ring {
-  static_assert(!PAIR || P == 1, "pairs hold at most 64 rows");
+  static_assert(!PAIR || P <= 2, "pairs hold at most 128 rows");
   static constexpr int kCG = PAIR ? 2 : 1;             // column groups per item
   static constexpr int kTokScaleOff = 64 * P * kKS;
-  static constexpr int kWOff = kTokScaleOff + kCG * kBM * 4;
+  static constexpr int kTokScaleBytes = PAIR ? 256 * P : kBM * 4;
+  static constexpr int kWOff = kTokScaleOff + kTokScaleBytes;
   static constexpr int kWScaleOff = kWOff + kCG * kBN * kKS / 2;
   static constexpr int kStage = kWScaleOff + kCG * kBN * 4;
   static constexpr int kNumBuf = PAIR ? 3 : P == 4 ? 3 : P == 2 ? 4 : 5;
@@ -105,10 +108,12 @@ struct Ring {
   static constexpr int kTileStep = PAIR ? 2 : 4;       // between a wavefront's token tiles
   static constexpr int kBytes = kNumBuf * kStage;
 };
-constexpr int kRingBytes = Ring<4>::kBytes;   // 153600, the largest of the four
-static_assert(Ring<2>::kBytes <= kRingBytes && Ring<1>::kBytes <= kRingBytes &&
-              Ring<1, true>::kBytes <= kRingBytes, "ring");
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int kRingBytes = cmax(cmax(Ring<4>::kBytes, Ring<2>::kBytes),
+                                cmax(cmax(Ring<1>::kBytes, Ring<1, true>::kBytes),
+                                     Ring<2, true>::kBytes));   // 155136 (Ring<2, true>)
 static_assert((Ring<1>::kAhead - 1) * Ring<1>::kLoads < 64, "vmcnt");
+static_assert(Ring<2, true>::kLoads <= 8, "load slots");
 constexpr int kLdsBytes = kRingBytes + 8 * (kMaxLdsExperts + 1) + 16;
 static_assert(kLdsBytes <= 160 * 1024, "LDS");
 
@@ -158,17 +163,19 @@ struct AOp {
 // writes its per-XCD item ranges.
 // Items of one FC launch, split over the 8 XCDs by estimated work: an item
 // (expert e, column group, 256-row tile) costs about kItemFixedRows + its rows
-// rounded up to 16 per stage.  An expert with at most 64 rows has n_cg / 2
-// items (each two column groups), one with more n_cg items per 256-row tile.
+// rounded up to 16 per stage.  An expert with at most kPairRows rows has
+// n_cg / 2 items (each two column groups), one with more n_cg items per
+// 256-row tile.
 // Workgroup 0 of the pre-pass scans the per-expert work and item counts,
 // writes the item prefix over the experts to item_prefix[0..E_local] and the
 // first item of each XCD's range (at a column-group boundary) to
 // bounds[0..8].
 constexpr int kItemFixedRows = 64;
+constexpr int kPairRows = 128;  // experts with at most this many rows run as pair items
 constexpr int kTileGroup = 4;   // tiles per item group of a multi-tile expert
 
 __device__ __forceinline__ int expert_items(int rows, int n_tiles, int n_cg) {
-  return rows == 0 ? 0 : rows <= 64 ? n_cg / 2 : n_tiles * n_cg;
+  return rows == 0 ? 0 : rows <= kPairRows ? n_cg / 2 : n_tiles * n_cg;
 }
 
 __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __restrict__ prefix,
@@ -241,7 +248,7 @@ __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __r
       const long long per_cg = nt > 0 ? (cum_s[e + 1] - cum_s[e]) / n_cg : 1;
       long long cg = per_cg > 0 ? (target - cum_s[e]) / per_cg : 0;
       cg = cg < n_cg ? cg : n_cg;
-      item = items_s[e] + (c <= 64 ? (int)cg / 2 : (int)cg * nt);
+      item = items_s[e] + (c <= kPairRows ? (int)cg / 2 : (int)cg * nt);
     }
     bounds[tid] = item;
   }
@@ -358,7 +365,7 @@ __device__ __forceinline__ void prefill_item(const FcParams& p, uint8_t* lds, co
     else if (!PAIR || q == P + nw)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s_r, base + s_lds, 4, s_voff, s_step * sc, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_r, base + RG::kTokScaleOff + 256 * wave, 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t_r, base + RG::kTokScaleOff + 256 * (wave % P), 4,
                                                t_voff, t_step * sc, 0, 0);
   };
 
@@ -489,12 +496,20 @@ __device__ __forceinline__ void prefill_item(const FcParams& p, uint8_t* lds, co
     }
   };
   // At most 64 P rows in use make at most 4 P tiles, so a wavefront
-  // holds at most P of them (with PAIR, at most 2).
-  if constexpr (PAIR) {
+  // holds at most P of them (with PAIR, at most 2 P).
+  if constexpr (PAIR && P == 1) {
     switch (nj) {
       case 0: run(std::integral_constant<int, 0>{}); break;
       case 1: run(std::integral_constant<int, 1>{}); break;
       default: run(std::integral_constant<int, 2>{}); break;
+    }
+  } else if constexpr (PAIR) {
+    switch (nj) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
     }
   } else if constexpr (P == 1) {
     if (nj == 0) run(std::integral_constant<int, 0>{});
@@ -565,11 +580,11 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     if (item >= item_hi || item < item_lo) break;
     const int e = __builtin_amdgcn_readfirstlane(find_expert_lds(prefix_s, p.E_local, item));
     const int local = item - __builtin_amdgcn_readfirstlane(prefix_s[e]);
-    // An expert with at most 64 rows (one tile) runs as pairs of column
-    // groups: its item i takes column groups 2 i and 2 i + 1.
+    // An expert with at most kPairRows rows runs as pairs of column groups:
+    // its item i takes column groups 2 i and 2 i + 1.
     const int e_rows = __builtin_amdgcn_readfirstlane(offs_s[e + 1]) -
                        __builtin_amdgcn_readfirstlane(offs_s[e]);
-    const bool pair = e_rows <= 64;
+    const bool pair = e_rows <= kPairRows;
     const int nt = (e_rows + kBM - 1) / kBM;
     // Items of an expert run in groups of kTileGroup tiles: within a group,
     // column group by column group, tile by tile.  The items in flight then
@@ -603,7 +618,7 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     // two column groups' 32 pieces (column group c / 16).  Scale dwords:
     // wavefronts 0..3 copy token rows 64 w + l, wavefronts 4..7 weight rows
     // 64 (w - 4) + l; of a pair, wavefront w copies weight rows 64 w + l of
-    // the two column groups' 512 and token rows 64 w + l.
+    // the two column groups' 512 and token rows 64 (w % P) + l.
     __amdgpu_buffer_rsrc_t w_r, s_r, t_r = act_r;
     uint32_t w_voff[4] = {0u, 0u, 0u, 0u}, s_voff, t_voff = kOutOfRange;
     int w_step, s_step, t_step = 0;
@@ -637,7 +652,9 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     if (pair) {
       t_r = st_r;
       t_step = st_step;
-      const int tok = 64 * wave + lane;
+      // Wavefront w copies token rows 64 (w % P) + l (P = 1 or 2 pieces
+      // of 64 rows; the wavefronts with equal w % P write the same bytes).
+      const int tok = 64 * (wave % (rows_used <= 64 ? 1 : 2)) + lane;
       t_voff = tok < rows_used ? 4u * (uint32_t)(row_begin + tok) : kOutOfRange;
     }
     if (!pair && wave < 4) {
@@ -670,8 +687,12 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
       const int c = wave >> 2;
       const LaneGeom lg{wave, lane, hw, th, g, li, a_lo - 2048 * (qt - th), a_hi - 2048 * (qt - th),
                         a_sc - 64 * (qt - th), b_op + 16384 * c, b_sc + 1024 * c};
-      prefill_item<FC1, TILED, 1, true>(p, lds, lg, it, act_r, w_r, s_r, t_r, w_voff, s_voff,
-                                        t_voff, w_step, s_step, t_step);
+      if (rows_used <= 64)
+        prefill_item<FC1, TILED, 1, true>(p, lds, lg, it, act_r, w_r, s_r, t_r, w_voff, s_voff,
+                                          t_voff, w_step, s_step, t_step);
+      else
+        prefill_item<FC1, TILED, 2, true>(p, lds, lg, it, act_r, w_r, s_r, t_r, w_voff, s_voff,
+                                          t_voff, w_step, s_step, t_step);
     } else {
       const LaneGeom lg{wave, lane, hw, qt, g, li, a_lo, a_hi, a_sc, b_op, b_sc};
       if (rows_used <= 64)
