@@ -174,8 +174,16 @@ constexpr int kItemFixedRows = 64;
 constexpr int kPairRows = 128;  // experts with at most this many rows run as pair items
 constexpr int kTileGroup = 4;   // tiles per item group of a multi-tile expert
 
+// Items of an expert with more than kPairRows rows run in groups of
+// kTileGroup tiles, the last group (1..kTileGroup tiles) holding the last
+// tile; when that tile has at most kPairRows rows it runs as pair items, each
+// after the other tiles' items of its two column groups.
 __device__ __forceinline__ int expert_items(int rows, int n_tiles, int n_cg) {
-  return rows == 0 ? 0 : rows <= kPairRows ? n_cg / 2 : n_tiles * n_cg;
+  if (rows == 0) return 0;
+  if (rows <= kPairRows) return n_cg / 2;
+  const int full = (n_tiles - 1) / kTileGroup, rem = n_tiles - full * kTileGroup;
+  const bool tail_pair = rows - kBM * (n_tiles - 1) <= kPairRows;
+  return full * kTileGroup * n_cg + (tail_pair ? (n_cg / 2) * (2 * rem - 1) : n_cg * rem);
 }
 
 __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __restrict__ prefix,
@@ -248,7 +256,8 @@ __device__ void split_items(const int32_t* __restrict__ offs, const int32_t* __r
       const long long per_cg = nt > 0 ? (cum_s[e + 1] - cum_s[e]) / n_cg : 1;
       long long cg = per_cg > 0 ? (target - cum_s[e]) / per_cg : 0;
       cg = cg < n_cg ? cg : n_cg;
-      item = items_s[e] + (c <= kPairRows ? (int)cg / 2 : (int)cg * nt);
+      // The expert's items in proportion (any item boundary will do).
+      item = items_s[e] + (int)((long long)(items_s[e + 1] - items_s[e]) * cg / n_cg);
     }
     bounds[tid] = item;
   }
@@ -584,27 +593,43 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     // its item i takes column groups 2 i and 2 i + 1.
     const int e_rows = __builtin_amdgcn_readfirstlane(offs_s[e + 1]) -
                        __builtin_amdgcn_readfirstlane(offs_s[e]);
-    const bool pair = e_rows <= kPairRows;
     const int nt = (e_rows + kBM - 1) / kBM;
-    // Items of an expert run in groups of kTileGroup tiles: within a group,
-    // column group by column group, tile by tile.  The items in flight then
-    // cover about 8 column groups x 4 tiles of a hot expert (its weights
-    // shared by 4 tiles, each tile's rows by 8 column groups) instead of
-    // 3 column groups x 10 tiles, which needs fewer bytes from memory.
-    const int full = nt / kTileGroup, in_full = n_cg * kTileGroup * full;
-    int cg, t_in_e;
+    // Items of a larger expert run in groups of kTileGroup tiles: within a
+    // group, column group by column group, tile by tile.  The items in
+    // flight then cover about 8 column groups x 4 tiles of a hot expert (its
+    // weights shared by 4 tiles, each tile's rows by 8 column groups) instead
+    // of 3 column groups x 10 tiles, which needs fewer bytes from memory.
+    // The last group (1..kTileGroup tiles) holds the last tile; one of at
+    // most kPairRows rows is a pair item after the other tiles' items of its
+    // two column groups (their weights still in L2).
+    const int full = (nt - 1) / kTileGroup, in_full = n_cg * kTileGroup * full;
+    int cg0, t_in_e;   // first column group, tile
+    bool pair = e_rows <= kPairRows;
     if (pair) {
-      cg = 2 * local + (wave >> 2);   // this wavefront's column group
+      cg0 = 2 * local;
       t_in_e = 0;
     } else if (local < in_full) {
       const int grp = local / (n_cg * kTileGroup), r = local - grp * n_cg * kTileGroup;
-      cg = r / kTileGroup;
-      t_in_e = grp * kTileGroup + (r - cg * kTileGroup);
+      cg0 = r / kTileGroup;
+      t_in_e = grp * kTileGroup + (r - cg0 * kTileGroup);
     } else {
       const int rem = nt - full * kTileGroup, r = local - in_full;
-      cg = r / rem;
-      t_in_e = full * kTileGroup + (r - cg * rem);
+      if (e_rows - kBM * (nt - 1) <= kPairRows) {
+        const int per = 2 * rem - 1, cgp = r / per, x = r - cgp * per;
+        if (x < 2 * (rem - 1)) {
+          cg0 = 2 * cgp + x / (rem - 1);
+          t_in_e = full * kTileGroup + x % (rem - 1);
+        } else {
+          cg0 = 2 * cgp;
+          t_in_e = nt - 1;
+          pair = true;
+        }
+      } else {
+        cg0 = r / rem;
+        t_in_e = full * kTileGroup + (r - cg0 * rem);
+      }
     }
+    const int cg = pair ? cg0 + (wave >> 2) : cg0;   // this wavefront's column group
     const int row_begin = __builtin_amdgcn_readfirstlane(offs_s[e]) + t_in_e * kBM;
     const int n_valid = min(__builtin_amdgcn_readfirstlane(offs_s[e + 1]) - row_begin, kBM);
     const int ntiles = (n_valid + 15) >> 4;                      // 16-row tiles in use
@@ -622,7 +647,6 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
     __amdgpu_buffer_rsrc_t w_r, s_r, t_r = act_r;
     uint32_t w_voff[4] = {0u, 0u, 0u, 0u}, s_voff, t_voff = kOutOfRange;
     int w_step, s_step, t_step = 0;
-    const int cg0 = pair ? 2 * local : cg;   // first column group of the item
     const int nwp = pair ? 4 : 2;            // weight pieces per wavefront
     if (TILED) {
       const size_t blk0 = tiled_block(e, cg0 >> 1, 0, n_cg >> 1, n_stages);

@@ -410,11 +410,12 @@ def test_one_hot_expert_spanning_many_tiles():
 @pytest.mark.parametrize("tiled", [True, False])
 def test_prefill_row_counts_at_layout_bounds(tiled):
     # Experts whose row counts sit on both sides of the prefill kernel's
-    # 16-row tile, 64 / 128-row stage layouts and 256-row item bounds (and
-    # experts of two and three items), their rows scattered over the tokens
-    # (K = 1).
+    # 16-row tile, 64 / 128-row stage layouts and pair items, and 256-row item
+    # bounds (and experts of two to five tiles, whose last tile of at most 128
+    # rows runs as pair items: 257, 320, 384, 513, 640, 868, 1064; or not:
+    # 385, 401, 700), their rows scattered over the tokens (K = 1).
     counts = [1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320,
-              384, 385, 401]
+              384, 385, 401, 513, 640, 700, 868, 1064]
     T = sum(counts)
     cfg = synth.custom_config("bounds", 307, T=T, H=512, I=256, E=len(counts), K=1)
     act, w_np, w_dev = _small_case(cfg)
