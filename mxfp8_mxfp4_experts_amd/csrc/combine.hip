@@ -54,7 +54,7 @@ __global__ __launch_bounds__(64) void combine_kernel(const uint16_t* __restrict_
       ex[j] = 0;
       if (rr[j] >= 0) {
         a[j] = *reinterpret_cast<const uint4*>(y + (size_t)rr[j] * H + (size_t)c * 8);
-        ex[j] = ye[(size_t)rr[j] * (H / 64) + (c >> 3)];
+        ex[j] = ye[ye_index(rr[j], c >> 3, H / 64)];
       }
     }
 #pragma unroll

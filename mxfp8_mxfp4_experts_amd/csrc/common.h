@@ -55,12 +55,22 @@ struct WsLayout {
                         // stage-major in grouped-row order (prefill-shaped FC kernels)
   size_t y;             // deterministic combine: fp16 [T * top_k][H] (FC2 rows before the
                         // combine, scaled); atomic combine: float [T][H] (the weighted sums)
-  size_t ye;            // deterministic combine: int8 [T * top_k][H / 64], the power-of-two
-                        // scale of each 64 columns (atomic combine: empty)
+  size_t ye;            // deterministic combine: int8, the power-of-two scale of each 64
+                        // columns of each y row, in blocks of 16 rows (ye_index; atomic
+                        // combine: empty)
   size_t total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Place of the scale exponent of columns [64 u, 64 u + 64) of y row `row`
+// (n_u = H / 64 per row): rows in blocks of 16, each block column-major, so
+// the 16 rows of an FC2 sub-tile write their exponents of one unit as one
+// 16-byte run, and the 8 consecutive units a combine wavefront reads for a
+// row lie in one 128-byte line.
+__host__ __device__ inline size_t ye_index(int64_t row, int u, int n_u) {
+  return ((size_t)(row >> 4) * n_u + u) * 16 + (size_t)(row & 15);
+}
 
 inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I, bool atomic = false) {
   WsLayout l;
@@ -78,7 +88,7 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I, bool atom
   off = atomic ? align256(off + sizeof(float) * (size_t)T * H)
                : align256(off + sizeof(uint16_t) * (size_t)T * top_k * H);
   l.ye = off;
-  off = atomic ? off : align256(off + (size_t)T * top_k * (H / 64));
+  off = atomic ? off : align256(off + ((size_t)T * top_k + 15) / 16 * 16 * (H / 64));
   l.total = off;
   return l;
 }

@@ -41,7 +41,7 @@ struct FcParams {
   uint8_t* hq;               // FC1 out [R, I]
   uint8_t* hs;               // FC1 out [R, I/32]
   uint16_t* y;               // FC2 out [R, N]: fp16 of y / 2^ye (deterministic combine)
-  int8_t* ye;                // FC2 out [R, N / 64]: scale exponent per 64 columns
+  int8_t* ye;                // FC2 out: scale exponent per 64 columns (ye_index)
   // Atomic combine (FC2 only; out_acc == nullptr otherwise): grouped row r
   // adds topk_w[route] * y[r] into out_acc[route / top_k] with
   // route = combine_route[r].
@@ -270,7 +270,7 @@ __device__ __forceinline__ void store_subtile(const FcParams& p, const v4f (&acc
       for (int s = 0; s < 2; ++s)
         *reinterpret_cast<uint4*>(dst + 32 * s) =
             uint4{d[2 * s][0], d[2 * s][1], d[2 * s + 1][0], d[2 * s + 1][1]};
-      if (g == 0) p.ye[(size_t)row * (p.N / 64) + u] = (int8_t)e;
+      if (g == 0) p.ye[ye_index(row, u, p.N / 64)] = (int8_t)e;
     }
   }
 }
