@@ -86,6 +86,10 @@ _ALL = [
 for _i, _m in enumerate((128, 512, 2048, 8192)):
     _ALL.append(LayerConfig(f"ckpt_ep32r7_M{_m}", 5 + _i, T=_m, H=3584, I=3072, E=896,
                             K=16, E_local=28, expert_offset=196, routing="ep_mixed"))
+# ... and the same shape at one token, the real-size decode case of the
+# pages' coverage matrix (page 1, "对称性约束").
+_ALL.append(LayerConfig("ckpt_ep32r7_M1", 9, T=1, H=3584, I=3072, E=896, K=16, E_local=28,
+                        expert_offset=196, routing="ep_mixed"))
 WORKLOADS = {c.name: c for c in _ALL}
 
 

@@ -967,8 +967,24 @@ def _ckpt_weights(cfg):
 
 @pytest.mark.parametrize("tiled", [True, False])
 def test_ckpt_shape_M128_all_tokens(tiled):
-    cfg = synth.WORKLOADS["ckpt_ep32r7_M128"]
-    print(f"[ckpt M128 tiled={tiled}] {cfg}", flush=True)
+    _ckpt_all_tokens(synth.WORKLOADS["ckpt_ep32r7_M128"], tiled, f"ckpt M128 tiled={tiled}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 8, 32])
+def test_ckpt_shape_small_M_all_tokens(M):
+    """The checkpoint-true shape at the token counts of the pages' coverage
+    matrix (page 1, "对称性约束": M = 1/2/8/32, and the real-size decode at
+    M = 1), every token against the oracle."""
+    if M == 1:
+        cfg = synth.WORKLOADS["ckpt_ep32r7_M1"]
+    else:
+        cfg = synth.custom_config(f"ckpt_M{M}", 330 + M, T=M, H=3584, I=3072, E=896, K=16,
+                                  E_local=28, expert_offset=196, routing="ep_mixed")
+    _ckpt_all_tokens(cfg, True, f"ckpt M{M}")
+
+
+def _ckpt_all_tokens(cfg, tiled, tag):
+    print(f"[{tag}] {cfg}", flush=True)
     act = synth.make_activations(cfg)
     w_dev = _ckpt_weights(cfg)
     w_np = {k: to_np(v) for k, v in w_dev.items()}
@@ -979,7 +995,7 @@ def test_ckpt_shape_M128_all_tokens(tiled):
     ref = oracle.oracle_layer(act["x_bf16"], None, None, w_np["w13"], w_np["w13_s"], w_np["w2"],
                               w_np["w2_s"], top_k=cfg.K, expert_offset=cfg.expert_offset,
                               topk_idx=act["topk_idx"], topk_w=act["topk_w"], report=True)
-    _check_full(cfg, act, res, ref, f"ckpt M128 tiled={tiled}", w_np)
+    _check_full(cfg, act, res, ref, tag, w_np)
 
 
 @pytest.mark.parametrize("name", ["ckpt_ep32r7_M512", "ckpt_ep32r7_M2048", "ckpt_ep32r7_M8192"])

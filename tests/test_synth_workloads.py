@@ -18,11 +18,25 @@ def test_ep_mixed_configs_match_the_pages_benchmark():
     f = _facts()["ep_mixed_benchmark"]
     ck = _facts()["ep_mapping"]
     cfgs = [c for c in synth.WORKLOADS.values() if c.routing == "ep_mixed"]
-    assert [c.T for c in cfgs] == f["M"]
+    assert [c.T for c in cfgs if c.T in f["M"]] == f["M"]
     for c in cfgs:
         assert (c.H, c.I, c.E, c.E_local, c.K) == (f["H"], f["I"], f["E"], f["E_local"], f["top_k"])
         assert c.E_local == ck["num_global"] // ck["ep"]
         assert c.expert_offset == f["ep_rank"] * c.E_local
+
+
+def test_ep_mixed_configs_cover_the_real_size_decode_and_prefill():
+    """The pages' coverage matrix runs the real-size shape at decode M = 1 and
+    prefill M = 128; both are workloads here, and the rest of the ep_mixed
+    workloads are the benchmark's batch sizes."""
+    cov = _facts()["coverage_matrix"]
+    bench = _facts()["ep_mixed_benchmark"]["M"]
+    cfgs = [c for c in synth.WORKLOADS.values() if c.routing == "ep_mixed"]
+    Ts = [c.T for c in cfgs]
+    assert cov["decode_M"] in Ts and cov["prefill_M"] in Ts
+    assert set(Ts) == set(bench) | {cov["decode_M"], cov["prefill_M"]}
+    for c in cfgs:
+        assert (c.H, c.I, c.E_local, c.K) == (cov["H"], cov["I"], cov["E_local"], cov["top_k"])
 
 
 def test_ep_mixed_routing_structure():
@@ -66,6 +80,7 @@ def test_workload_table_names_keys_and_shapes():
         "ckpt_ep32r7_M512": (6, 512, 3584, 3072, 896, 16, 28, 196),
         "ckpt_ep32r7_M2048": (7, 2048, 3584, 3072, 896, 16, 28, 196),
         "ckpt_ep32r7_M8192": (8, 8192, 3584, 3072, 896, 16, 28, 196),
+        "ckpt_ep32r7_M1": (9, 1, 3584, 3072, 896, 16, 28, 196),
     }
     assert list(synth.WORKLOADS) == list(want)
     for name, c in synth.WORKLOADS.items():
