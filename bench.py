@@ -230,28 +230,44 @@ def cpu_baseline(cfg, act, w_dev, rid, rw, runs):
     w = {k: np.stack([w_dev[k][int(e)].cpu().numpy() for e in touched])
          for k in ("w13", "w13_s", "w2", "w2_s")}
     x = act["x_bf16"][:n]
-    times = []
-    for _ in range(runs):
-        t0 = time.perf_counter()
-        if given:
-            sid, sw = ids, rw[:n]
-        else:
-            sid, sw = oracle.route(act["logits"][:n], act["bias"], cfg.K, cfg.routed_scaling)
-        cid = np.where(keep, remap[np.clip(local, 0, cfg.E_local - 1)], -1).astype(np.int32)
-        assert given or np.array_equal(sid, ids)
-        oracle.oracle_layer(x, None, None, w["w13"], w["w13_s"], w["w2"], w["w2_s"],
-                            top_k=cfg.K, expert_offset=0, alpha=cfg.situ_alpha,
-                            beta=cfg.situ_beta, topk_idx=cid, topk_w=sw)
-        times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
+
+    def timed(n_runs):
+        times = []
+        for _ in range(n_runs):
+            t0 = time.perf_counter()
+            if given:
+                sid, sw = ids, rw[:n]
+            else:
+                sid, sw = oracle.route(act["logits"][:n], act["bias"], cfg.K, cfg.routed_scaling)
+            cid = np.where(keep, remap[np.clip(local, 0, cfg.E_local - 1)], -1).astype(np.int32)
+            assert given or np.array_equal(sid, ids)
+            oracle.oracle_layer(x, None, None, w["w13"], w["w13_s"], w["w2"], w["w2_s"],
+                                top_k=cfg.K, expert_offset=0, alpha=cfg.situ_alpha,
+                                beta=cfg.situ_beta, topk_idx=cid, topk_w=sw)
+            times.append(time.perf_counter() - t0)
+        return float(np.median(times))
+
+    dt = timed(runs)
     hr = host_record()
-    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": hr["blas_threads"],
-            "kind": "oracle", "host_cores": hr["host_cores"], "cpu_model": hr["cpu_model"],
-            "runs": runs, "seconds_per_run": round(dt, 3),
-            "sample": f"the first {n} tokens of the workload ({int(keep.sum())} kept routes, "
-                      f"{len(touched)} experts); oracle.route + oracle.oracle_layer (steps "
-                      f"O1-O8, float64), weights of the touched experts copied to host first; "
-                      f"median of {runs} run(s)"}
+    rec = {"value": round(n / dt, 4), "unit": "tokens/s", "cores": hr["blas_threads"],
+           "kind": "oracle", "host_cores": hr["host_cores"], "cpu_model": hr["cpu_model"],
+           "runs": runs, "seconds_per_run": round(dt, 3),
+           "sample": f"the first {n} tokens of the workload ({int(keep.sum())} kept routes, "
+                     f"{len(touched)} experts); oracle.route + oracle.oracle_layer (steps "
+                     f"O1-O8, float64), weights of the touched experts copied to host first; "
+                     f"median of {runs} run(s)"}
+    if cfg.T <= 16:
+        # Small batches: the same sample once more with the BLAS pool held to
+        # one thread (the oracle's other steps are single-threaded NumPy).
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                dt1 = timed(1)
+            rec["one_thread"] = {"value": round(n / dt1, 4), "unit": "tokens/s",
+                                 "seconds_per_run": round(dt1, 3), "runs": 1}
+        except ImportError:
+            pass
+    return rec
 
 
 # ---------------------------------------------------------------------------
