@@ -151,12 +151,14 @@ __device__ __forceinline__ void super_steps(v4f (&acc)[NT][4], const uint8_t* co
 }
 
 // One tile of NT 16-row subtiles [row_begin, row_end) of expert e against
-// column group cg (one unit per wavefront).  stream_w: the expert has this one
-// tile, so its weights are read once and streamed past the caches.
+// unit 4 cg + wave of column group cg (one unit per wavefront; the
+// wavefronts of a column group share nothing, so they may sit in one
+// workgroup or in four).  stream_w: the expert has this one tile, so its
+// weights are read once and streamed past the caches.
 template <bool FC1, int NT, bool TILED, int SJ = 2, bool ACC_A = false>
-__device__ __forceinline__ void fc_tile(const FcParams& p, int e, int cg, int row_begin,
+__device__ __forceinline__ void fc_tile(const FcParams& p, int e, int cg, int wave, int row_begin,
                                         int row_end, bool stream_w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   const int u = cg * 4 + wave;
   if (u >= p.n_units) return;
   const int g = lane >> 4, li = lane & 15;

@@ -37,16 +37,20 @@ static_assert(kDecodeTilePrefixIndex == kMapTileIndex, "tile map");
 // path, a larger one the two-subtile path, so an expert with 17..32 rows reads
 // its weights once and one with fewer does no empty MFMAs.  Two wavefronts per
 // SIMD (256 VGPRs at most): one's weight stream is in flight while the
-// other's MFMAs issue.
-template <bool FC1, bool TILED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fc_kernel(
+// other's MFMAs issue.  WAVES wavefronts per workgroup: 4 (a column group's
+// units) or, for a grid that would leave CUs idle, 1 (each unit its own
+// workgroup, so the same wavefronts spread over every CU).
+template <bool FC1, bool TILED, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2))) void fc_kernel(
     FcParams p) {
   // Consecutive block ids land on different XCDs (round robin over 8); remap
   // so that each XCD walks a contiguous range of (column group, tile) items,
   // with the tiles of one expert adjacent and sharing its weights in L2.
   const int nb = gridDim.x, b = blockIdx.x;
   const int logical = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  const int cg = logical / p.max_tiles, tile = logical % p.max_tiles;
+  const int group = logical / p.max_tiles, tile = logical % p.max_tiles;
+  const int cg = WAVES == 4 ? group : group >> 2;
+  const int wave = WAVES == 4 ? (int)(threadIdx.x >> 6) : (group & 3);
   const int* prefix = p.tile_prefix;
   if (tile >= prefix[p.E_local]) return;
   const int e = p.tile_map[tile];
@@ -54,9 +58,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int row_end = min(p.expert_offsets[e + 1], row_begin + kDecodeTileRows);
   const bool stream_w = prefix[e + 1] - prefix[e] == 1;
   if (row_end - row_begin <= 16)
-    fc_tile<FC1, 1, TILED>(p, e, cg, row_begin, row_end, stream_w);
+    fc_tile<FC1, 1, TILED>(p, e, cg, wave, row_begin, row_end, stream_w);
   else
-    fc_tile<FC1, 2, TILED>(p, e, cg, row_begin, row_end, stream_w);
+    fc_tile<FC1, 2, TILED>(p, e, cg, wave, row_begin, row_end, stream_w);
 }
 
 int expected_rows(int R, int E_local) {
@@ -77,12 +81,22 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_
   const int groups = (prm.n_units + 3) / 4;
   const int64_t blocks = (int64_t)groups * prm.max_tiles;
   if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(256);
-  if (tiled)
-    hipLaunchKernelGGL((fc_kernel<FC1, true>), grid, block, 0, stream, prm);
-  else
-    hipLaunchKernelGGL((fc_kernel<FC1, false>), grid, block, 0, stream, prm);
+  if (4 * blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  // Fewer than two four-wavefront workgroups per CU (at most max_tiles
+  // tiles, a bound): one workgroup per unit instead.
+  if (blocks < 2 * (int64_t)n_cu) {
+    const dim3 grid((unsigned)(4 * blocks)), block(64);
+    if (tiled)
+      hipLaunchKernelGGL((fc_kernel<FC1, true, 1>), grid, block, 0, stream, prm);
+    else
+      hipLaunchKernelGGL((fc_kernel<FC1, false, 1>), grid, block, 0, stream, prm);
+  } else {
+    const dim3 grid((unsigned)blocks), block(256);
+    if (tiled)
+      hipLaunchKernelGGL((fc_kernel<FC1, true, 4>), grid, block, 0, stream, prm);
+    else
+      hipLaunchKernelGGL((fc_kernel<FC1, false, 4>), grid, block, 0, stream, prm);
+  }
   return hipGetLastError();
 }
 
