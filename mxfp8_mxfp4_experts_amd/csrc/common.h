@@ -47,7 +47,8 @@ inline int perm_chunks(int64_t R) {
 struct WsLayout {
   size_t tile_prefix;   // int32 [kNumTileSizes][E_local + 1], then the tile -> expert map
                         // int32 [tile_map_entries(T * top_k, E_local)]
-  size_t perm_counts;   // int32 [perm_chunks(R)][E_local] (grouping scratch)
+  size_t perm_counts;   // int32 [perm_chunks(R)][E_local], then [E_local] expert totals
+                        // (grouping scratch)
   size_t fc_sched;      // int32 [9][kSchedStride]: per-XCD work counters of the prefill FC
                         // kernels, then their 9 item-range bounds; then int32 [E_local + 1]:
                         // the prefix of the experts' work items
@@ -79,7 +80,7 @@ inline WsLayout ws_layout(int T, int top_k, int E_local, int H, int I, bool atom
   off = align256(off + sizeof(int32_t) * (kNumTileSizes * (size_t)(E_local + 1) +
                                           (size_t)tile_map_entries((int64_t)T * top_k, E_local)));
   l.perm_counts = off;
-  off = align256(off + sizeof(int32_t) * (size_t)perm_chunks((int64_t)T * top_k) * E_local);
+  off = align256(off + sizeof(int32_t) * ((size_t)perm_chunks((int64_t)T * top_k) + 1) * E_local);
   l.fc_sched = off;
   off = align256(off + sizeof(int32_t) * (kSchedItemPrefix + E_local + 1));
   l.act_st = off;

@@ -16,10 +16,11 @@
 // wavefront its own slice when a per-wavefront count table fits in LDS, else
 // one wavefront all of them).
 // Large batches: the routes are cut into chunks (perm_chunk_size); a count
-// kernel writes each chunk's histogram, one workgroup turns the histograms
-// into expert offsets, tile prefixes and each chunk's first row per expert,
-// and a rank kernel (one wavefront per chunk) runs the ballot ranking on its chunk from
-// those starting rows.
+// kernel writes each chunk's histogram, a column-scan kernel (one workgroup
+// per 64 experts) turns each expert's chunk counts into the chunks' first rows
+// within the expert and the expert's total, one workgroup scans the totals
+// into expert offsets and tile prefixes, and a rank kernel (one wavefront per
+// chunk) runs the ballot ranking on its chunk from those starting rows.
 #include "common.h"
 #include "launch.h"
 #include "permute_dev.h"
@@ -64,11 +65,52 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e < E_local; e += 256) counts[(size_t)c * E_local + e] = cnt_s[e];
 }
 
-// Chunk histograms -> per-chunk starting rows (in place), expert offsets,
-// tile prefixes; grouped rows past the kept count get -1.
+// Chunk histograms -> each chunk's first row within the expert (in place)
+// and each expert's total.  Workgroup b takes experts [64 b, 64 b + 64), one
+// per lane; each of its kColWaves wavefronts sums its share of the chunks
+// (loads of 64 consecutive experts are one coalesced run), the shares' sums
+// give each wavefront its starting row, then it rewrites its chunks.
 constexpr int kBatch = 16;
+constexpr int kColWaves = 16;
+__global__ __launch_bounds__(64 * kColWaves) void perm_colscan_kernel(
+    int E_local, int n_chunks, int32_t* __restrict__ counts, int32_t* __restrict__ totals) {
+  __shared__ int part_s[kColWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const bool ok = e < E_local;
+  const int per = (n_chunks + kColWaves - 1) / kColWaves;
+  const int c0 = min(w * per, n_chunks), c1 = min(c0 + per, n_chunks);
+  int sum = 0;
+  for (int c = c0; c < c1; c += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      v[j] = ok && c + j < c1 ? counts[(size_t)(c + j) * E_local + e] : 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) sum += v[j];
+  }
+  part_s[w][lane] = sum;
+  __syncthreads();
+  int row = 0;
+  for (int i = 0; i < w; ++i) row += part_s[i][lane];
+  if (w == kColWaves - 1 && ok) totals[e] = row + sum;
+  for (int c = c0; c < c1; c += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      v[j] = ok && c + j < c1 ? counts[(size_t)(c + j) * E_local + e] : 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (ok && c + j < c1) counts[(size_t)(c + j) * E_local + e] = row;
+      row += v[j];
+    }
+  }
+}
+
+// Expert totals -> expert offsets, tile prefixes and the tile -> expert map;
+// grouped rows past the kept count get -1.
 __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
-    int R, int E_local, int n_chunks, int32_t* __restrict__ counts,
+    int R, int E_local, const int32_t* __restrict__ totals,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_route,
     int32_t* __restrict__ tile_prefix) {
   __shared__ int wave_tot[kPermWaves][kScanVals];
@@ -81,17 +123,7 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
 #pragma unroll
   for (int v = 0; v < kScanVals; ++v) local[v] = 0;
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
-    // Chunk counts in batches of kBatch loads in flight (the chunks of one
-    // expert are a dependent chain otherwise).
-    int total = 0;
-    for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
-      int v[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        v[j] = c0 + j < n_chunks ? counts[(size_t)(c0 + j) * E_local + e] : 0;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) total += v[j];
-    }
+    const int total = totals[e];
     local[0] += total;
 #pragma unroll
     for (int i = 0; i < kNumTileSizes; ++i) local[1 + i] += tiles_of(total, i);
@@ -126,25 +158,13 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   int excl[kScanVals];
 #pragma unroll
   for (int v = 0; v < kScanVals; ++v) excl[v] = incl[v] - local[v] + wave_tot[wave][v];
-  // Then each expert's offset, its chunks' absolute starting rows, its
-  // tile prefixes and its entries of the tile -> expert map.
+  // Then each expert's offset, its tile prefixes and its entries of the
+  // tile -> expert map.
   int32_t* const tile_map = tile_prefix + kNumTileSizes * (E_local + 1);
   for (int e = e0; e < e0 + per && e < E_local; ++e) {
     expert_offsets[e] = excl[0];
-    int row = excl[0];
-    for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
-      int v[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        v[j] = c0 + j < n_chunks ? counts[(size_t)(c0 + j) * E_local + e] : 0;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if (c0 + j < n_chunks) counts[(size_t)(c0 + j) * E_local + e] = row;
-        row += v[j];
-      }
-    }
-    const int total = row - excl[0];
-    excl[0] = row;
+    const int total = totals[e];
+    excl[0] += total;
 #pragma unroll
     for (int i = 0; i < kNumTileSizes; ++i) {
       tile_prefix[i * (E_local + 1) + e] = excl[1 + i];
@@ -158,15 +178,18 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(
   for (int r = n_kept + tid; r < R; r += kPermThreads) sorted_route[r] = -1;
 }
 
-// Step 3 on one chunk, from the chunk's starting rows.
+// Step 3 on one chunk, from the chunk's starting rows (within the expert,
+// plus the expert's offset).
 __global__ __launch_bounds__(64) void perm_rank_kernel(const int32_t* __restrict__ idx, int R,
                                                        int offset, int E_local, int chunk,
                                                        const int32_t* __restrict__ starts,
+                                                       const int32_t* __restrict__ expert_offsets,
                                                        int32_t* __restrict__ sorted_route,
                                                        int32_t* __restrict__ route_row) {
   extern __shared__ int cursor_s[];
   const int c = blockIdx.x, lane = threadIdx.x;
-  for (int e = lane; e < E_local; e += 64) cursor_s[e] = starts[(size_t)c * E_local + e];
+  for (int e = lane; e < E_local; e += 64)
+    cursor_s[e] = starts[(size_t)c * E_local + e] + expert_offsets[e];
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < E_local) ++nbits;
@@ -219,10 +242,13 @@ hipError_t launch_permute(const int32_t* idx, int R, int offset, int E_local, in
   const size_t lds = sizeof(int) * (size_t)E_local;
   hipLaunchKernelGGL(perm_count_kernel, dim3(n_chunks), dim3(256), lds, stream, idx, R, offset,
                      E_local, chunk, counts);
+  int32_t* const totals = counts + (size_t)n_chunks * E_local;
+  hipLaunchKernelGGL(perm_colscan_kernel, dim3((E_local + 63) / 64), dim3(64 * kColWaves), 0, stream,
+                     E_local, n_chunks, counts, totals);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(kPermThreads), 0, stream, R, E_local,
-                     n_chunks, counts, offs, sorted_route, tile_prefix);
+                     totals, offs, sorted_route, tile_prefix);
   hipLaunchKernelGGL(perm_rank_kernel, dim3(n_chunks), dim3(64), lds, stream, idx, R, offset,
-                     E_local, chunk, counts, sorted_route, route_row);
+                     E_local, chunk, counts, offs, sorted_route, route_row);
   return hipGetLastError();
 }
 
