@@ -38,9 +38,24 @@ __global__ __launch_bounds__(kPermThreads) void front_kernel(
   int* cnt = ids + T * K;                                // [E_local]
   int* cursor = cnt + E_local;                           // [E_local]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < T * E; i += kPermThreads) {
-    const int t = i / E, e = i - t * E;
-    keys[i] = ordered_key(sigmoid_score(logits[(size_t)t * ld + e]) + (bias ? bias[e] : 0.0f));
+  // Up to 16 keys per thread (T * E <= 16 * 1024): all of a thread's logits
+  // and biases are loaded before its first sigmoid, so their latencies
+  // overlap instead of adding up.
+  {
+    constexpr int kKeysPerThread = 16;
+    float lv[kKeysPerThread], bv[kKeysPerThread];
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+      const int i = tid + j * kPermThreads;
+      const int t = i / E, e = i - t * E;
+      lv[j] = i < T * E ? logits[(size_t)t * ld + e] : 0.0f;
+      bv[j] = i < T * E && bias ? bias[e] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kKeysPerThread; ++j) {
+      const int i = tid + j * kPermThreads;
+      if (i < T * E) keys[i] = ordered_key(sigmoid_score(lv[j]) + bv[j]);
+    }
   }
   __syncthreads();
   if (wave < T) {
