@@ -320,9 +320,8 @@ class Run:
         sroute, rrow = layer.sorted_route[:R], layer.route_row[:R]
         hq, hs = layer.hq[:R], layer.hs[:R]
         if self.given:
-            B.moe_quant_mxfp8(self.x, xq, xs)
-            B.moe_permute(idx, cfg.expert_offset, cfg.E_local, layer.workspace,
-                          layer.expert_offsets, sroute, rrow)
+            B.moe_quant_permute(self.x, idx, cfg.expert_offset, cfg.E_local, layer.workspace,
+                                xq, xs, layer.expert_offsets, sroute, rrow)
         else:
             B.moe_route_quant_permute(self.logits, self.bias, K, cfg.routed_scaling, self.x,
                                       cfg.expert_offset, cfg.E_local, layer.workspace, idx, tw,

@@ -4,7 +4,8 @@
  *
  * The layer (one GPU's share of a Kimi-K3-style routed-expert MoE) is five
  * calls, issued in this order on one HIP stream (the first three can also be
- * issued as one, moe_route_quant_permute):
+ * issued as one, moe_route_quant_permute; with top-k ids computed elsewhere,
+ * the second and third as one, moe_quant_permute):
  *
  *   moe_route        sigmoid + correction-bias top-k routing, renormalised weights
  *   moe_quant_mxfp8  bf16 activations -> MXFP8 (E4M3 + one E8M0 scale per 32)
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Status codes have fixed values (page 1 records a Python/C++ enum mismatch
  * that silently turned SiTU into a non-gated activation; these values never
@@ -189,6 +190,21 @@ moe_status_t moe_route_quant_permute(const float* logits, int64_t ld_logits, con
                                      uint8_t* xs, int32_t* expert_offsets, int32_t* sorted_route,
                                      int32_t* route_row, void* workspace, size_t ws_bytes,
                                      hipStream_t stream);
+
+/* a2 + a3 in one call, for top-k ids and weights computed before the expert
+ * layer (page 1 "Serving call chain": the fused MoE call receives the router's
+ * top-k ids and weights; its Phase 4 benchmark feeds them in directly).
+ * Computes exactly what moe_quant_mxfp8 and then moe_permute compute with the
+ * same arguments (same bytes in every output and in the workspace), and
+ * accepts what those two accept together (every check of each).  When the
+ * grouping runs as one workgroup (T * top_k <= 2048) it is a single launch,
+ * workgroup 0 grouping while the others quantise; otherwise it issues the two
+ * calls' launches in order on `stream`. */
+moe_status_t moe_quant_permute(const uint16_t* x, int64_t ld_x, int T, int H,
+                               const int32_t* topk_idx, int top_k, int expert_offset,
+                               int E_local, uint8_t* xq, uint8_t* xs, int32_t* expert_offsets,
+                               int32_t* sorted_route, int32_t* route_row, void* workspace,
+                               size_t ws_bytes, hipStream_t stream);
 
 /* a4 + a5 + a6 -- FC1 grouped GEMM, SiTU, requantisation (page 1 "Serving call
  * chain": grouped GEMM1 then gated activation; "Real checkpoint contract": w13

@@ -3,7 +3,8 @@
 The layer is five C calls into ``libmi355moe.so`` (declared in
 ``include/mi355moe.h``); this package is their thin Python binding plus
 ``MoELayer``, which issues the calls in order with one workspace (routing,
-quantisation and grouping as the one call ``moe_route_quant_permute``).
+quantisation and grouping as the one call ``moe_route_quant_permute``; with
+given top-k ids, quantisation and grouping as ``moe_quant_permute``).
 """
 from ._binding import (  # noqa: F401
     COMBINE_ATOMIC,
@@ -24,6 +25,7 @@ from ._binding import (  # noqa: F401
     moe_prepack_w13_layout,
     moe_prepack_w2,
     moe_quant_mxfp8,
+    moe_quant_permute,
     moe_route,
     moe_route_quant_permute,
     moe_workspace_size,

@@ -28,7 +28,7 @@ EXPORTS = (
     "moe_abi_version", "moe_strerror", "moe_workspace_size", "moe_route", "moe_quant_mxfp8",
     "moe_permute", "moe_fc1_situ", "moe_fc2_combine", "moe_prepack_w13", "moe_prepack_w2",
     "moe_fc1_situ_tiled", "moe_fc2_combine_tiled", "moe_route_quant_permute",
-    "moe_prepack_w13_layout", "moe_permute_noalloc",
+    "moe_prepack_w13_layout", "moe_permute_noalloc", "moe_quant_permute",
 )
 
 # moe_w13_layout_t values (row order of a w13 tensor)
@@ -63,6 +63,9 @@ def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
     lib.moe_permute.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]
     lib.moe_permute_noalloc.restype = _I
     lib.moe_permute_noalloc.argtypes = [_P, _I, _I, _I, _I, _P, _P, _P, _P]
+    lib.moe_quant_permute.restype = _I
+    lib.moe_quant_permute.argtypes = [_P, _I64, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                                      _SZ, _P]
     lib.moe_route_quant_permute.restype = _I
     lib.moe_route_quant_permute.argtypes = [_P, _I64, _P, _I, _I, _I, _F, _P, _I64, _I, _I, _I,
                                             _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
@@ -259,6 +262,46 @@ def moe_permute(topk_idx: torch.Tensor, expert_offset: int, E_local: int, worksp
                                             _ptr(route_row), _ptr(workspace), workspace.numel(),
                                             _stream()))
     return expert_offsets, sorted_route, route_row
+
+
+def moe_quant_permute(x: torch.Tensor, topk_idx: torch.Tensor, expert_offset: int, E_local: int,
+                      workspace: torch.Tensor, xq=None, xs=None, expert_offsets=None,
+                      sorted_route=None, route_row=None):
+    """moe_quant_mxfp8 and moe_permute as one call (same results), for top-k
+    ids computed elsewhere."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [T, H] with unit column stride")
+    xb = x if x.dtype == torch.uint16 else (x.view(torch.uint16) if x.dtype == torch.bfloat16 else None)
+    if xb is None:
+        raise ValueError(f"x must be bfloat16 (or uint16 bf16 bits), got {x.dtype}")
+    _need(xb, "x", torch.uint16, contiguous=False)
+    _need(topk_idx, "topk_idx", torch.int32, device=x.device)
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != x.shape[0]:
+        raise ValueError("topk_idx must be [T, top_k] with the rows of x")
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    dev = x.device
+    _need(workspace, "workspace", torch.uint8, device=dev)
+    if xq is None:
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    if xs is None:
+        xs = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    if expert_offsets is None:
+        expert_offsets = torch.empty(E_local + 1, dtype=torch.int32, device=dev)
+    if sorted_route is None:
+        sorted_route = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if route_row is None:
+        route_row = torch.empty(T * K, dtype=torch.int32, device=dev)
+    _need(xq, "xq", torch.uint8, (T, H), device=dev)
+    _need(xs, "xs", torch.uint8, (T, H // 32), device=dev)
+    _need(expert_offsets, "expert_offsets", torch.int32, (E_local + 1,), device=dev)
+    _need(sorted_route, "sorted_route", torch.int32, (T * K,), device=dev)
+    _need(route_row, "route_row", torch.int32, (T * K,), device=dev)
+    _check("moe_quant_permute", lib().moe_quant_permute(
+        _ptr(xb), x.stride(0), T, H, _ptr(topk_idx), K, expert_offset, E_local, _ptr(xq),
+        _ptr(xs), _ptr(expert_offsets), _ptr(sorted_route), _ptr(route_row), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return xq, xs, expert_offsets, sorted_route, route_row
 
 
 def moe_permute_noalloc(topk_idx: torch.Tensor, expert_offset: int, E_local: int,

@@ -181,6 +181,38 @@ moe_status_t moe_route_quant_permute(const float* logits, int64_t ld_logits, con
                                sorted_route, route_row, prefix, counts, stream));
 }
 
+moe_status_t moe_quant_permute(const uint16_t* x, int64_t ld_x, int T, int H,
+                               const int32_t* topk_idx, int top_k, int expert_offset,
+                               int E_local, uint8_t* xq, uint8_t* xs, int32_t* expert_offsets,
+                               int32_t* sorted_route, int32_t* route_row, void* workspace,
+                               size_t ws_bytes, hipStream_t stream) {
+  // The checks of moe_quant_mxfp8 and moe_permute.
+  if (T < 0 || H < 32 || H % 32 != 0 || ld_x < H || (int64_t)T * H > ((int64_t)1 << 40))
+    return MOE_ERR_SHAPE;
+  if (!valid_window(top_k, E_local) || expert_offset < 0 ||
+      (int64_t)T * top_k > ((int64_t)1 << 30))
+    return MOE_ERR_SHAPE;
+  if (!expert_offsets || !workspace) return MOE_ERR_NULL;
+  if (T > 0 && (!x || !xq || !xs || !topk_idx || !sorted_route || !route_row)) return MOE_ERR_NULL;
+  if (!aligned(expert_offsets, 4) || !aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  if (T > 0 && (!aligned(x, 16) || ld_x % 8 != 0 || !aligned(xq, 16) || !aligned(xs, 4) ||
+                !aligned(topk_idx, 4) || !aligned(sorted_route, 4) || !aligned(route_row, 4)))
+    return MOE_ERR_ALIGN;
+  if (ws_bytes < ws_layout(T, top_k, E_local, 0, 0).y) return MOE_ERR_WORKSPACE;
+  moe_status_t s = check_device();
+  if (s != MOE_OK) return s;
+  WsLayout l = ws_layout(T, top_k, E_local, 0, 0);
+  int32_t* prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.tile_prefix);
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + l.perm_counts);
+  if (T > 0 && quant_permute_fusable(T * top_k))
+    return finish(launch_quant_permute(x, ld_x, T, H, xq, xs, topk_idx, T * top_k, expert_offset,
+                                       E_local, expert_offsets, sorted_route, route_row, prefix,
+                                       stream));
+  if (T > 0 && launch_quant(x, ld_x, T, H, xq, xs, stream) != hipSuccess) return MOE_ERR_HIP;
+  return finish(launch_permute(topk_idx, T * top_k, expert_offset, E_local, expert_offsets,
+                               sorted_route, route_row, prefix, counts, stream));
+}
+
 static moe_status_t fc1_impl(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
                           int E_local, const int32_t* expert_offsets,
                           const int32_t* sorted_route, const uint8_t* w13,

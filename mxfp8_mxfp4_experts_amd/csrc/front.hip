@@ -75,6 +75,23 @@ __global__ __launch_bounds__(kPermThreads) void front_kernel(
                 sorted_route, route_row, tile_prefix, cnt, cursor, ids, nullptr);
 }
 
+// a2 + a3 for given top-k ids: workgroup 0 groups the routes (the
+// single-workgroup grouping, as permute_kernel), the others quantise.
+__global__ __launch_bounds__(kPermThreads) void quant_permute_kernel(
+    const uint16_t* __restrict__ x, int64_t ld_x, int T, int H, uint8_t* __restrict__ xq,
+    uint8_t* __restrict__ xs, const int32_t* __restrict__ idx, int R, int offset, int E_local,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_route,
+    int32_t* __restrict__ route_row, int32_t* __restrict__ tile_prefix) {
+  if (blockIdx.x > 0) {
+    quant_piece(x, ld_x, T, H, xq, xs, (int64_t)(blockIdx.x - 1) * kPermThreads + threadIdx.x);
+    return;
+  }
+  extern __shared__ int lds_i[];
+  permute_block([&](int r) { return idx[r]; }, R, offset, E_local, expert_offsets, sorted_route,
+                route_row, tile_prefix, lds_i, lds_i + E_local, lds_i + 2 * E_local,
+                E_local <= kPermWaveTableExperts ? lds_i + 2 * E_local + R : nullptr);
+}
+
 size_t front_lds_bytes(int T, int E, int K, int E_local) {
   return sizeof(int) * ((size_t)T * E + (size_t)T * K + 2 * (size_t)E_local);
 }
@@ -97,6 +114,24 @@ hipError_t launch_front(const float* logits, int64_t ld, const float* bias, int 
                      front_lds_bytes(T, E, K, E_local), stream, logits, ld, bias, T, E, K, scaling,
                      topk_idx, topk_w, x, ld_x, H, xq, xs, offset, E_local, offs, sorted_route,
                      route_row, tile_prefix);
+  return hipGetLastError();
+}
+
+bool quant_permute_fusable(int64_t R) { return R >= 1 && R <= kPermSingle; }
+
+hipError_t launch_quant_permute(const uint16_t* x, int64_t ld_x, int T, int H, uint8_t* xq,
+                                uint8_t* xs, const int32_t* idx, int R, int offset, int E_local,
+                                int32_t* offs, int32_t* sorted_route, int32_t* route_row,
+                                int32_t* tile_prefix, hipStream_t stream) {
+  // LDS of the single-workgroup grouping (as launch_permute sizes it).
+  const size_t table = E_local <= kPermWaveTableExperts ? (size_t)kPermWaves * E_local : 0;
+  const size_t lds = sizeof(int) * (2 * (size_t)E_local + (size_t)R + table);
+  const int64_t pieces = (int64_t)T * (H / 8);
+  const int64_t blocks = 1 + (pieces + kPermThreads - 1) / kPermThreads;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(quant_permute_kernel, dim3((unsigned)blocks), dim3(kPermThreads), lds, stream,
+                     x, ld_x, T, H, xq, xs, idx, R, offset, E_local, offs, sorted_route, route_row,
+                     tile_prefix);
   return hipGetLastError();
 }
 

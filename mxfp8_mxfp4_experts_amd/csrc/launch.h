@@ -23,6 +23,14 @@ hipError_t launch_front(const float* logits, int64_t ld, const float* bias, int 
                         int64_t ld_x, int H, uint8_t* xq, uint8_t* xs, int offset, int E_local,
                         int32_t* offs, int32_t* sorted_route, int32_t* route_row,
                         int32_t* tile_prefix, hipStream_t stream);
+// Quantise + group in one launch (front.hip), when the grouping is one
+// workgroup (R <= kPermSingle); the same bytes as launch_quant and
+// launch_permute.
+bool quant_permute_fusable(int64_t R);
+hipError_t launch_quant_permute(const uint16_t* x, int64_t ld_x, int T, int H, uint8_t* xq,
+                                uint8_t* xs, const int32_t* idx, int R, int offset, int E_local,
+                                int32_t* offs, int32_t* sorted_route, int32_t* route_row,
+                                int32_t* tile_prefix, hipStream_t stream);
 hipError_t launch_fc1(const uint8_t* xq, const uint8_t* xs, int T, int H, int I, int top_k,
                       int E_local, const int32_t* offs, const int32_t* sorted_route,
                       const uint8_t* w13, const uint8_t* w13_s, float alpha, float beta,

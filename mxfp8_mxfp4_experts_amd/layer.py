@@ -108,9 +108,9 @@ class MoELayer:
                                       self.route_row[:R])
         else:
             idx, w = topk_idx, topk_w
-            B.moe_quant_mxfp8(x, xq, xs)
-            B.moe_permute(idx, self.expert_offset, self.E_local, self.workspace,
-                          self.expert_offsets, self.sorted_route[:R], self.route_row[:R])
+            # quantisation and grouping as one call
+            B.moe_quant_permute(x, idx, self.expert_offset, self.E_local, self.workspace, xq, xs,
+                                self.expert_offsets, self.sorted_route[:R], self.route_row[:R])
         B.moe_fc1_situ(xq, xs, K, self.expert_offsets, self.sorted_route[:R], self.w13,
                        self.w13_s, self.workspace, self.alpha, self.beta, self.hq[:R],
                        self.hs[:R], tiled=self.tiled)

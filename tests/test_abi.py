@@ -40,7 +40,7 @@ def test_library_exports_every_header_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     for code in (0, 1, 2, 3, 4, 5, 6, 7, 8):
         assert lib.moe_strerror(code)
     assert lib.moe_strerror(99) == b"unknown status"
@@ -119,6 +119,33 @@ def test_route_quant_permute_validation(lib):
     assert call(offs=None) == 1
     assert call(x=FAKE + 8) == 3          # x not 16-aligned
     assert call(ld_x=132) == 3            # ld_x % 8
+    assert call(ws=FAKE + 16) == 3        # workspace alignment
+    assert call(wsb=8) == 5               # workspace too small
+
+
+def test_quant_permute_validation(lib):
+    f = lib.moe_quant_permute
+
+    def call(**kw):
+        a = dict(x=FAKE, ld_x=128, T=4, H=128, idx=FAKE, k=2, off=0, el=8, xq=FAKE, xs=FAKE,
+                 offs=FAKE, sr=FAKE, rr=FAKE, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return f(a["x"], a["ld_x"], a["T"], a["H"], a["idx"], a["k"], a["off"], a["el"], a["xq"],
+                 a["xs"], a["offs"], a["sr"], a["rr"], a["ws"], a["wsb"], None)
+
+    assert call(k=0) == 2                 # top_k
+    assert call(H=100, ld_x=128) == 2     # H % 32
+    assert call(ld_x=64) == 2             # ld_x < H
+    assert call(off=-1) == 2              # expert offset
+    assert call(el=0) == 2                # E_local
+    assert call(T=-1) == 2
+    assert call(x=None) == 1
+    assert call(idx=None) == 1
+    assert call(offs=None) == 1
+    assert call(ws=None) == 1
+    assert call(x=FAKE + 8) == 3          # x not 16-aligned
+    assert call(ld_x=132) == 3            # ld_x % 8
+    assert call(idx=FAKE + 2) == 3        # topk_idx not 4-aligned
     assert call(ws=FAKE + 16) == 3        # workspace alignment
     assert call(wsb=8) == 5               # workspace too small
 

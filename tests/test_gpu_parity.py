@@ -267,6 +267,43 @@ def test_route_quant_permute_matches_separate_calls(T, E, K, E_local, offset, H)
     assert ulp.max() <= 4, "routing weights with routed_scaling"
 
 
+@pytest.mark.parametrize("T,K,E,E_local,offset,H,masked", [
+    (1, 16, 896, 28, 196, 3584, False),    # checkpoint-true decode, one token (one launch)
+    (128, 16, 896, 28, 196, 3584, False),  # checkpoint M = 128: 2048 routes (one launch)
+    (8, 16, 896, 896, 0, 7168, True),      # masked slots, the full expert set (one launch)
+    (40, 8, 256, 64, 10, 512, True),       # an EP window (one launch)
+    (300, 16, 896, 28, 196, 256, False),   # 4800 routes: the two calls' launches
+])
+def test_quant_permute_matches_separate_calls(T, K, E, E_local, offset, H, masked):
+    """moe_quant_permute gives the bytes of moe_quant_mxfp8 and moe_permute
+    called one after the other, for given top-k ids (grouping also against
+    the oracle)."""
+    m = _lib()
+    rng = np.random.default_rng(2000 + T * 7 + E_local)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :K].astype(np.int32)
+    if masked:
+        ids[rng.random((T, K)) < 0.2] = -1
+    x = synth.f32_to_bf16_bits((0.5 * rng.standard_normal((T, H))).astype(np.float32))
+    print(f"[quant_permute] T={T} K={K} E_local={E_local} offset={offset} H={H}", flush=True)
+    d_ids = torch.from_numpy(ids).to(DEV)
+    d_x = torch.from_numpy(x.astype(np.int16)).to(DEV).view(torch.bfloat16)
+    nbytes = m.moe_workspace_size(T, K, E_local, 128, 128)
+    ws_a = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    ws_b = torch.full((nbytes,), 0x55, dtype=torch.uint8, device=DEV)
+    xq_a, xs_a = m.moe_quant_mxfp8(d_x)
+    offs_a, sr_a, rr_a = m.moe_permute(d_ids, offset, E_local, ws_a)
+    xq_b, xs_b, offs_b, sr_b, rr_b = m.moe_quant_permute(d_x, d_ids, offset, E_local, ws_b)
+    torch.cuda.synchronize()
+    for name, a, b in (("xq", xq_a, xq_b), ("xs", xs_a, xs_b), ("expert_offsets", offs_a, offs_b),
+                       ("sorted_route", sr_a, sr_b), ("route_row", rr_a, rr_b)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+    _check_tile_schedule(ws_b, np.diff(to_np(offs_b)), E_local)
+    r_offs, r_sr, r_rr = oracle.permute(ids, offset, E_local)
+    assert np.array_equal(to_np(offs_b), r_offs)
+    assert np.array_equal(to_np(sr_b)[:r_offs[-1]], r_sr)
+    assert np.array_equal(to_np(rr_b), r_rr)
+
+
 @pytest.mark.parametrize("layout", ["up_gate", "interleaved"])
 def test_prepack_w13_layouts(layout):
     """w13 in [up; gate] halves or interleaved gate/up rows (page 1, real
