@@ -336,6 +336,35 @@ class Run:
                           layer.w2_s, layer.workspace, self.out, tiled=layer.tiled,
                           mode=layer.combine_mode)
 
+    def time_graph(self, layer, steps):
+        """The same step captured once in a HIP graph (the five calls are
+        capturable: no allocation, synchronisation or memset node) and replayed
+        `steps` times between two events: the step without the per-call host
+        and launch costs that bound the smallest batches."""
+        import torch
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.step(layer)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(layer)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / steps
+        del g
+        return ms
+
     def time_steps(self, layer, steps, warmup, fc1_every=4):
         """W untimed steps, then exactly `steps` steps between two events,
         bracketed by synchronisations.  Every `fc1_every`-th step also records
@@ -457,6 +486,11 @@ def finish_run(run, round_times, args, with_cpu, cpu_runs):
                 topk_w=layer.topk_w[:cfg.T].clone() if run.given else None)
     if not torch.equal(ref.view(torch.int16), det.view(torch.int16)):
         raise SystemExit(f"[bench] {name}: timed path disagrees with MoELayer")
+    graph_ms = None
+    if not args.no_graph:
+        graph_ms = run.time_graph(layer, args.steps)
+        if not torch.equal(run.out.view(torch.int16), det.view(torch.int16)):
+            raise SystemExit(f"[bench] {name}: graph replay disagrees with the eager step")
     atomic_ms = None
     if not args.no_atomic:
         alayer = layer.with_combine("atomic")
@@ -470,6 +504,9 @@ def finish_run(run, round_times, args, with_cpu, cpu_runs):
         del alayer
         torch.cuda.empty_cache()
     rec = workload_record(run, ms, fc1_ms, wall, atomic_ms)
+    if graph_ms is not None:
+        rec["graph"] = {"ms_per_step": round(graph_ms, 5),
+                        "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 2)}
     if len(round_times) > 1:
         r_ms = [r[0] for r in round_times]
         rec["rounds"] = {"n": len(r_ms), "ms_per_step": [round(v, 5) for v in r_ms],
@@ -495,6 +532,7 @@ def main():
                          "turn; a workload's step time is the median of its rounds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-atomic", action="store_true", help="skip the atomic-combine timing")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     ap.add_argument("--no-rates", action="store_true", help="skip the achievable-rate probes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
@@ -555,7 +593,7 @@ def main():
     if "cpu_baseline" in head:
         res["cpu_baseline"] = head["cpu_baseline"]
     res["layer"] = head["layer"]
-    for k in ("combine_atomic", "pages_ratio", "rounds"):
+    for k in ("combine_atomic", "graph", "pages_ratio", "rounds"):
         if k in head:
             res[k] = head[k]
     if len(names) > 1:
