@@ -53,7 +53,11 @@ __global__ __launch_bounds__(64) void combine_kernel(const uint16_t* __restrict_
       a[j] = uint4{0u, 0u, 0u, 0u};
       ex[j] = 0;
       if (rr[j] >= 0) {
-        a[j] = *reinterpret_cast<const uint4*>(y + (size_t)rr[j] * H + (size_t)c * 8);
+        // Each row piece is read once: a non-temporal load.
+        typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+        const u4v v = __builtin_nontemporal_load(
+            reinterpret_cast<const u4v*>(y + (size_t)rr[j] * H + (size_t)c * 8));
+        a[j] = uint4{v.x, v.y, v.z, v.w};
         ex[j] = ye[ye_index(rr[j], c >> 3, H / 64)];
       }
     }
