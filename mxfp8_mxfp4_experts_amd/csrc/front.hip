@@ -37,6 +37,8 @@ __global__ __launch_bounds__(kPermThreads) void front_kernel(
   int* ids = lds_i + T * E;                              // [T * K]
   int* cnt = ids + T * K;                                // [E_local]
   int* cursor = cnt + E_local;                           // [E_local]
+  // [T][64] selection candidates, 8-byte aligned after the int arrays
+  uint64_t* cand = reinterpret_cast<uint64_t*>(lds_i + ((T * E + T * K + 2 * E_local + 1) & ~1));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Up to 16 keys per thread (T * E <= 16 * 1024): all of a thread's logits
   // and biases are loaded before its first sigmoid, so their latencies
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(kPermThreads) void front_kernel(
   if (wave < T) {
     int id;
     float w;
-    select_topk_wave(keys + wave * E, logits + (size_t)wave * ld, E, K, scaling, lane, id, w);
+    select_topk_wave(keys + wave * E, logits + (size_t)wave * ld, E, K, scaling, lane,
+                     cand + 64 * wave, id, w);
     if (lane < K) {
       topk_idx[(size_t)wave * K + lane] = id;
       topk_w[(size_t)wave * K + lane] = w;
@@ -93,7 +96,8 @@ __global__ __launch_bounds__(kPermThreads) void quant_permute_kernel(
 }
 
 size_t front_lds_bytes(int T, int E, int K, int E_local) {
-  return sizeof(int) * ((size_t)T * E + (size_t)T * K + 2 * (size_t)E_local);
+  return sizeof(int) * ((((size_t)T * E + (size_t)T * K + 2 * (size_t)E_local + 1) & ~(size_t)1) +
+                        2 * 64 * (size_t)T);
 }
 
 }  // namespace

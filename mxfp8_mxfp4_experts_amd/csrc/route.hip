@@ -8,10 +8,14 @@
 // expert index.
 //  * E <= 1024: one workgroup per token computes the keys (as
 //    order-preserving unsigned integers) into LDS; then lane l of the first
-//    wavefront holds the keys of experts l, l + 64, ... in registers.  Each of
-//    the K rounds takes the lane's best remaining key, the wavefront maximum
-//    of those (DPP row shifts and broadcasts), then the smallest expert index
-//    among the lanes holding that maximum; the owning lane retires the winner.
+//    wavefront holds the keys of experts l, l + 64, ... in registers.  The
+//    K-th largest of the lanes' own largest keys bounds the selected keys
+//    from below; the keys that reach it (usually few) are sorted across the
+//    wavefront (key descending, then expert ascending) and lane k takes the
+//    k-th.  With more than 64 such keys (many ties) K rounds select instead:
+//    each takes the lane's best remaining key, the wavefront maximum of those
+//    (DPP row shifts and broadcasts), then the smallest expert index among
+//    the lanes holding that maximum; the owning lane retires the winner.
 //  * larger E: the keys sit in LDS and each round takes a wavefront arg-max
 //    over a 64-bit key (ordered float key, then inverted expert index)
 //    restricted to keys below the previous winner.
@@ -29,6 +33,7 @@ __global__ __launch_bounds__(256) void route_reg_kernel(
     const float* __restrict__ logits, int64_t ld, const float* __restrict__ bias, int T, int E,
     int K, float scaling, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   __shared__ uint32_t keys_s[64 * kRegExpertsPerLane];
+  __shared__ uint64_t cand_s[64];
   const int t = blockIdx.x;
   const float* row = logits + (size_t)t * ld;
   for (int e = threadIdx.x; e < E; e += 256)
@@ -38,7 +43,7 @@ __global__ __launch_bounds__(256) void route_reg_kernel(
   const int lane = threadIdx.x;
   int id;
   float w;
-  select_topk_wave(keys_s, row, E, K, scaling, lane, id, w);
+  select_topk_wave(keys_s, row, E, K, scaling, lane, cand_s, id, w);
   if (lane < K) {
     topk_idx[(size_t)t * K + lane] = id;
     topk_w[(size_t)t * K + lane] = w;

@@ -78,19 +78,18 @@ __device__ __forceinline__ Top2 lane_top2(const uint32_t (&key)[kRegExpertsPerLa
   return t;
 }
 
-// One wavefront selects the top K of one token (E <= 64 * kRegExpertsPerLane)
-// from its keys in LDS.  Lane l holds the keys of experts l, l + 64, ... and a
+// Top K of one token by rounds (E <= 64 * kRegExpertsPerLane), from its
+// keys in LDS.  Lane l holds the keys of experts l, l + 64, ... and a
 // cache of its best two remaining ones (key descending, expert ascending).
 // Each of the K rounds takes the wavefront maximum of the lanes' best keys
 // (DPP row shifts and broadcasts); the expert is read from the one lane
 // holding it, or, when several lanes hold that key, is the smallest expert
 // among them (a second reduction).  The owning lane retires the winner and
 // promotes its second key; only a lane that wins again before its cache is
-// refilled rescans its keys.  Lane k < K returns slot k's expert and weight
-// (s_k / sum_j s_j in double, times scaling).  Every lane must call this.
-__device__ __forceinline__ void select_topk_wave(const uint32_t* keys_s, const float* row, int E,
-                                                 int K, float scaling, int lane, int& id_out,
-                                                 float& w_out) {
+// refilled rescans its keys.  Lane k < K returns slot k's expert.  Every lane
+// must call this.
+__device__ __forceinline__ int select_topk_rounds(const uint32_t* keys_s, int E, int K,
+                                                  int lane) {
   uint32_t key[kRegExpertsPerLane];
   uint32_t avail = 0;                                // bit j: expert lane + 64 j not yet taken
 #pragma unroll
@@ -134,6 +133,95 @@ __device__ __forceinline__ void select_topk_wave(const uint32_t* keys_s, const f
     }
     if (lane == k) my_id = (int)win;
   }
+  return my_id;
+}
+
+// Descending bitonic sort of one value per lane across the wavefront: lane i
+// ends with the i-th largest.  In the stage merging blocks of k lanes at
+// distance j, lane i keeps the larger of the pair when bit k and bit j of i
+// agree (so the final k = 64 stage leaves the larger values in lower lanes).
+__device__ __forceinline__ uint32_t wave_sort_desc_u32(uint32_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t o = (uint32_t)__shfl_xor((int)v, j);
+      const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+      v = keep_max ? umax32(v, o) : umin32(v, o);
+    }
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_sort_desc_u64(uint64_t v, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j);
+      const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v, j);
+      const uint64_t o = ((uint64_t)ohi << 32) | olo;
+      const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+      v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  return v;
+}
+
+// The top K of one token by a threshold and two wavefront sorts, for the
+// usual case of few keys near the K-th largest.  T0, the K-th largest of the
+// 64 lanes' largest keys, is at most the K-th largest key (K lanes hold a key
+// of at least T0), so every selected key is at least T0.  Those candidates
+// (the key, then the inverted expert index, as one 64-bit value: key
+// descending, expert ascending) are gathered through cand (64 entries of LDS
+// per wavefront) and sorted, and lane k takes the k-th.  Returns false,
+// having selected nothing, when more than 64 keys reach T0 (many equal keys);
+// the rounds then select.  Every lane must call this.
+__device__ __forceinline__ bool select_topk_threshold(const uint32_t* keys_s, int E, int K,
+                                                      int lane, uint64_t* cand, int& my_id) {
+  uint32_t key[kRegExpertsPerLane];
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < kRegExpertsPerLane; ++j) {
+    const int e = lane + 64 * j;
+    key[j] = e < E ? keys_s[e] : 0u;   // 0: no expert (every real key is above 0)
+    m = umax32(m, key[j]);
+  }
+  const uint32_t t0 =
+      (uint32_t)__builtin_amdgcn_readlane((int)wave_sort_desc_u32(m, lane), K - 1);
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kRegExpertsPerLane; ++j) cnt += key[j] >= t0 && key[j] != 0u ? 1 : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  if (total > 64) return false;
+  int pos = incl - cnt;
+#pragma unroll
+  for (int j = 0; j < kRegExpertsPerLane; ++j)
+    if (key[j] >= t0 && key[j] != 0u)
+      cand[pos++] = ((uint64_t)key[j] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * j));
+  // The wavefront's LDS writes before its reads of other lanes' entries.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t c = wave_sort_desc_u64(lane < total ? cand[lane] : 0ull, lane);
+  my_id = (int)(0xFFFFFFFFu - (uint32_t)c);
+  return true;
+}
+
+// One wavefront selects the top K of one token (E <= 64 * kRegExpertsPerLane)
+// from its keys in LDS, ordered by key descending with ties to the lower
+// expert: by the threshold selection, else by rounds.  Lane k < K returns
+// slot k's expert and weight (s_k / sum_j s_j in double, times scaling).
+// cand: 64 entries of LDS for this wavefront.  Every lane must call this.
+__device__ __forceinline__ void select_topk_wave(const uint32_t* keys_s, const float* row, int E,
+                                                 int K, float scaling, int lane, uint64_t* cand,
+                                                 int& id_out, float& w_out) {
+  int my_id = 0;
+  if (!select_topk_threshold(keys_s, E, K, lane, cand, my_id))
+    my_id = select_topk_rounds(keys_s, E, K, lane);
   my_id = (my_id >= 0 && my_id < E) ? my_id : 0;
   const float my_s = lane < K ? sigmoid_score(row[my_id]) : 0.0f;
   double total = 0.0;
