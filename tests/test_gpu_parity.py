@@ -529,6 +529,25 @@ def test_route_ties_and_order():
         assert np.array_equal(to_np(w), rw)
 
 
+def test_route_many_ties_at_the_threshold():
+    """More than 64 keys at the selection threshold (equal keys across the
+    expert set) take the round-based selection; one row of distinct keys the
+    threshold path.  Both against the oracle, bit for bit."""
+    m = _lib()
+    T, E, K = 4, 896, 16
+    rng = np.random.default_rng(11)
+    logits = np.zeros((T, E), np.float32)                 # row 0: all equal
+    logits[1] = rng.standard_normal(E).astype(np.float32)
+    logits[1, rng.choice(E, 100, replace=False)] = 3.0    # 100 equal largest keys
+    logits[2] = rng.standard_normal(E).astype(np.float32)  # distinct keys
+    logits[3, ::5] = 1.0                                  # 180 equal largest keys
+    print("[route ties] T=4 E=896 K=16", flush=True)
+    ids, w = m.moe_route(torch.from_numpy(logits).to(DEV), None, K, 1.0)
+    rid, rw = oracle.route(logits, None, K, 1.0)
+    assert np.array_equal(to_np(ids), rid)
+    assert np.array_equal(to_np(w), rw)
+
+
 def test_route_strided_logits_and_full_width():
     m = _lib()
     rng = np.random.default_rng(11)
