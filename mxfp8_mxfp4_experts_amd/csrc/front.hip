@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kPermThreads) void front_kernel(
     quant_piece(x, ld_x, T, H, xq, xs, (int64_t)(blockIdx.x - 1) * kPermThreads + threadIdx.x);
     return;
   }
-  extern __shared__ int lds_i[];
+  extern __shared__ __attribute__((aligned(16))) int lds_i[];   // 16-byte aligned base
   uint32_t* keys = reinterpret_cast<uint32_t*>(lds_i);   // [T][E]
   int* ids = lds_i + T * E;                              // [T * K]
   int* cnt = ids + T * K;                                // [E_local]
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kPermThreads) void quant_permute_kernel(
     quant_piece(x, ld_x, T, H, xq, xs, (int64_t)(blockIdx.x - 1) * kPermThreads + threadIdx.x);
     return;
   }
-  extern __shared__ int lds_i[];
+  extern __shared__ __attribute__((aligned(16))) int lds_i[];
   permute_block([&](int r) { return idx[r]; }, R, offset, E_local, expert_offsets, sorted_route,
                 route_row, tile_prefix, lds_i, lds_i + E_local, lds_i + 2 * E_local,
                 E_local <= kPermWaveTableExperts ? lds_i + 2 * E_local + R : nullptr);
