@@ -1,8 +1,8 @@
 // One tile of up to 32 grouped rows of one expert against a group of
 // 64-row weight units, one unit per wavefront, with the weights streamed
 // straight from memory into registers (no LDS): the decode-shaped FC kernel
-// (fc.hip) runs one such tile per workgroup, and the prefill-shaped kernel
-// (fc_prefill.hip) uses it for experts that hold at most 32 grouped rows.
+// (fc.hip) runs one such tile per unit of work (four wavefronts of one
+// workgroup, or four one-wavefront workgroups).
 //
 // MFMA operand layout (16x16x128, one wavefront; pinned by a one-hot probe of
 // the instruction): A = weights in E2M1 (cbsz 4), B = activations in E4M3
