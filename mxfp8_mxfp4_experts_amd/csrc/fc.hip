@@ -43,16 +43,24 @@ static_assert(kDecodeTilePrefixIndex == kMapTileIndex, "tile map");
 template <bool FC1, bool TILED, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2))) void fc_kernel(
     FcParams p) {
-  // Consecutive block ids land on different XCDs (round robin over 8); remap
-  // so that each XCD walks a contiguous range of (column group, tile) items,
-  // with the tiles of one expert adjacent and sharing its weights in L2.
+  // Consecutive block ids land on different XCDs (round robin over 8).  The
+  // items are the (launch group, tile) pairs of the n tiles in use, group by
+  // group; XCD x walks items [x W / 8, (x + 1) W / 8) of the W = groups * n,
+  // so every XCD gets the same share of the work however many of the grid's
+  // max_tiles tiles per group are in use, and the tiles of one expert stay
+  // adjacent, sharing its weights in L2.  max_tiles is a multiple of 8 and at
+  // least n, so each XCD's nb / 8 workgroups cover its share.
   const int nb = gridDim.x, b = blockIdx.x;
-  const int logical = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  const int group = logical / p.max_tiles, tile = logical % p.max_tiles;
+  const int n_groups = nb / p.max_tiles;
+  const int* prefix = p.tile_prefix;
+  const int n_tiles = prefix[p.E_local];
+  const int64_t W = (int64_t)n_groups * n_tiles;
+  const int xcd = b & 7, i = b >> 3;
+  const int lo = (int)(xcd * W / 8), hi = (int)((xcd + 1) * W / 8);
+  if (lo + i >= hi) return;
+  const int group = (lo + i) / n_tiles, tile = lo + i - group * n_tiles;
   const int cg = WAVES == 4 ? group : group >> 2;
   const int wave = WAVES == 4 ? (int)(threadIdx.x >> 6) : (group & 3);
-  const int* prefix = p.tile_prefix;
-  if (tile >= prefix[p.E_local]) return;
   const int e = p.tile_map[tile];
   const int row_begin = p.expert_offsets[e] + (tile - prefix[e]) * kDecodeTileRows;
   const int row_end = min(p.expert_offsets[e + 1], row_begin + kDecodeTileRows);
@@ -77,7 +85,9 @@ hipError_t launch_fc(FcParams prm, int R, const int32_t* tile_prefix_all, int n_
   prm.tile_prefix = tile_prefix_all + (size_t)kDecodeTilePrefixIndex * (prm.E_local + 1);
   prm.tile_map = tile_prefix_all + (size_t)kNumTileSizes * (prm.E_local + 1);
   const int touched = R < prm.E_local ? R : prm.E_local;
-  prm.max_tiles = R / kDecodeTileRows + touched;
+  // A bound on the tiles in use (each touched expert adds at most one partial
+  // tile), rounded up to a multiple of the 8 XCDs.
+  prm.max_tiles = (R / kDecodeTileRows + touched + 7) & ~7;
   const int groups = (prm.n_units + 3) / 4;
   const int64_t blocks = (int64_t)groups * prm.max_tiles;
   if (blocks <= 0) return hipSuccess;
