@@ -561,9 +561,11 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
   }
   __syncthreads();
   const int xcd = blockIdx.x & 7;
-  const int item_lo = p.sched[8 * kSchedStride + xcd];
-  const int item_hi = p.sched[8 * kSchedStride + xcd + 1];
-  int32_t* const ctr = p.sched + xcd * kSchedStride;
+  // Ranges a workgroup may take items from: its own XCD's, then, when the
+  // launch has at least 8 rounds of items, the other XCDs' in turn (below).
+  const int32_t* const bounds = p.sched + 8 * kSchedStride;
+  const int n_ranges = bounds[8] - bounds[0] >= 8 * (int)gridDim.x ? 8 : 1;
+  int victim = 0;   // thread 0: the range it claims from is XCD xcd + victim's
   const __amdgpu_buffer_rsrc_t act_r = rsrc(p.act, (uint32_t)(p.act_rows * K));
 
   // LDS read offsets within a stage (lane parts; the tile's part and the
@@ -581,12 +583,32 @@ void fc_prefill_kernel(FcParams p, int n_cg) {
   // The workgroups of one XCD take its items in order from a shared counter,
   // so the items in flight are always a short run of neighbours (the column
   // groups of one tile, reading the same token rows from L2) however long
-  // each item takes.
+  // each item takes.  Over many rounds the ranges' estimated work can leave
+  // an XCD a round or more behind the rest, so a workgroup whose own range
+  // is exhausted goes on to the next XCDs' ranges, one after the other, and
+  // takes their next items (each item is still claimed exactly once, by the
+  // atomic on its range's counter, and nothing waits).  With fewer rounds
+  // every XCD reaches its last round at about the same time, and a taken
+  // item would only move to a CU whose L2 lacks its rows: then each
+  // workgroup keeps to its own range.
   for (;;) {
-    if (tid == 0) item_s[0] = item_lo + atomicAdd(ctr, 1);
+    if (tid == 0) {
+      int it = -1;
+      for (; victim < n_ranges; ++victim) {
+        const int x = (xcd + victim) & 7;
+        const int lo = bounds[x], hi = bounds[x + 1];
+        if (lo >= hi) continue;
+        const int c = lo + atomicAdd(p.sched + x * kSchedStride, 1);
+        if (c < hi) {
+          it = c;
+          break;
+        }
+      }
+      item_s[0] = it;
+    }
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(item_s[0]);
-    if (item >= item_hi || item < item_lo) break;
+    if (item < 0) break;
     const int e = __builtin_amdgcn_readfirstlane(find_expert_lds(prefix_s, p.E_local, item));
     const int local = item - __builtin_amdgcn_readfirstlane(prefix_s[e]);
     // An expert with at most kPairRows rows runs as pairs of column groups:
