@@ -61,16 +61,6 @@ def output_stats(out, ref):
                 rms=rms)
 
 
-def assert_output_close(out, ref, tag=""):
-    st = output_stats(out, ref)
-    print(f"[{tag}] max|err|/RMS={st['max_err_over_rms']:.4g} cosine={st['cosine']:.8f} "
-          f"bf16 floor={st['bf16_floor']:.4g}", flush=True)
-    assert np.all(np.isfinite(out))
-    assert (st["max_err_over_rms"] if raw else beyond) <= 2e-2, st
-    assert st["cosine"] >= 0.9995, st
-    return st
-
-
 # Bound on the block-scaled MFMA's accumulation error: one 16x16x128 MFMA
 # step adds at most ACC_EPS times the sum of |products| of its 128-K slice
 # (tests/test_gpu_numerics.py measures at most 8.9e-6, about 2^-16.8, for a

@@ -1007,6 +1007,38 @@ def test_full_size_single_token_decode():
                    [0], w_dev, "full T=1")
 
 
+@pytest.mark.parametrize("name", ["decode_T8", "batched_decode_T256", "prefill_T8192",
+                                  "ep_share_T4096"])
+def test_full_size_every_item_written(name):
+    """Every FC work item is done, however the workgroups divide the items
+    among themselves (across XCDs too): the FC1 output bytes, their scales and
+    the workspace (which holds FC2's rows) are first filled with codes that no
+    kernel writes (E4M3 and E8M0 NaN, fp16 NaN).  Afterwards no kept route row
+    of FC1 still holds one, every token's output is finite, and a second call
+    on the now-valid buffers returns the same bits."""
+    cfg = synth.WORKLOADS[name]
+    print(f"[every item {name}] {cfg}", flush=True)
+    w_all = full_size_weights()
+    sl = slice(cfg.expert_offset, cfg.expert_offset + cfg.E_local)
+    w_dev = {k: v[sl] for k, v in w_all.items()}
+    act = synth.make_activations(cfg)
+    layer = _layer_for(cfg, w_dev, cfg.T)
+    layer.hq.fill_(0x7F)
+    layer.hs.fill_(0xFF)
+    layer.workspace.fill_(0xFF)
+    torch.cuda.synchronize()
+    inputs = _device_inputs(act)
+    res = run_steps(layer, *inputs)
+    kept = int(res["expert_offsets"][-1])
+    print(f"[every item {name}] {kept} kept routes", flush=True)
+    assert kept > 0
+    assert not np.any((res["hq"][:kept] & 0x7F) == 0x7F), "FC1 output bytes left unwritten"
+    assert not np.any(res["hs"][:kept] == 0xFF), "FC1 output scales left unwritten"
+    assert np.all(np.isfinite(res["out"])), "outputs built from unwritten FC2 rows"
+    again = run_steps(layer, *inputs)
+    assert np.array_equal(again["out_bits"], res["out_bits"])
+
+
 # ---------------------------------------------------------------------------
 # The checkpoint-true expert shape with the pages' own benchmark routing
 # (28 local experts of 896, 8 local + 8 remote slots per token): top-k ids
